@@ -1,0 +1,206 @@
+/*
+ * kv4.h -- C ABI of libkv4: single-token decode attention over a paged,
+ * calibration-free INT4 KV cache with a bounded INT8 side cache for the
+ * attention-sink and recent positions, on AMD Instinct MI355X (gfx950).
+ *
+ * Sources (web pages; cited by title and section):
+ *   [NEWS] news summary "Async RL squeezes context into fewer decode steps;
+ *          INT4 KV cache speeds rollouts but loses accuracy, bounded INT8
+ *          protection recovers it": Synopsis; Interpretation paragraphs 1-4.
+ *   [ABS]  paper page "KV4-RL: Unlocking Faster Asynchronous Rollouts for RLVR
+ *          with INT4 KV Cache Quantization": The abstract; The Brief.
+ *   [ART]  news article on the same paper, section "INT4 as the base, INT8
+ *          insurance for critical positions".
+ *
+ * Conventions for every entry point
+ *   - Pointers are DEVICE pointers unless marked (host).  Structs passed by
+ *     pointer are host structs.
+ *   - Every call is asynchronous on `stream` and returns a kv4_status.  Host
+ *     argument checks happen before anything is launched; on an error nothing
+ *     is launched and nothing is written.  KV4_ERR_LAUNCH reports a failed
+ *     launch; faults inside a kernel surface at the caller's next stream sync.
+ *   - The caller allocates and owns every buffer (pools, side cache, page
+ *     table, lengths, q, out, lse, workspace).  The library allocates no
+ *     device memory and keeps no mutable global state; calls on different
+ *     streams are independent as long as they do not write the same pages,
+ *     side blocks, outputs or workspace.
+ *   - bf16 / fp16 values are passed as their raw 16-bit patterns (uint16_t).
+ *
+ * Cache layout (readings: the pages say only "paged INT4" plus an INT8 side
+ * cache of at most 144 positions, [NEWS] Interpretation para 3, [ART]):
+ *   pages: [num_pages][num_kv_heads][block_bytes]; a page holds 16
+ *          consecutive positions of one sequence (page_size = 16).
+ *   side:  [num_slots][num_kv_heads][side_bytes]; one side block per
+ *          sequence slot holds the INT8 copies of that sequence's protected
+ *          positions: sink position p < S in row p, later positions p >= S in
+ *          ring row S + ((p - S) mod R).
+ *   Quantization (calibration-free, [NEWS] Synopsis; [ABS] The abstract):
+ *   symmetric, scale = fp16(min(amax / qmax, 65504)) rounded to nearest even,
+ *   code = clamp(rint(x / scale), -qmax, qmax) with fp32 divides; INT4 per
+ *   (token, kv head, 32-channel group) with qmax 7, INT8 per (token, kv head)
+ *   with qmax 127.  The byte layout inside a block is documented next to
+ *   kv4_block_bytes below.
+ */
+#ifndef KV4_H
+#define KV4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KV4_ABI_VERSION 1
+
+typedef enum {
+  KV4_OK = 0,
+  KV4_ERR_INVALID_ARG = -1, /* null pointer, negative size, bad shape        */
+  KV4_ERR_UNSUPPORTED = -2, /* valid but not implemented (head_dim, page...) */
+  KV4_ERR_WORKSPACE = -3,   /* workspace smaller than *_workspace_size       */
+  KV4_ERR_LAUNCH = -4       /* the HIP runtime rejected a launch             */
+} kv4_status;
+
+/* Shapes (host).  Supported: head_dim 64 or 128, page_size 16, group_size 32,
+ * num_q_heads a multiple of num_kv_heads, n_sink >= 0, n_recent >= 0 and
+ * n_sink + n_recent <= 144 (the bound on the protected set, [NEWS]
+ * Interpretation para 3).  n_sink = n_recent = 0 is plain INT4 KV.  The kv8_
+ * and kvbf16_ entry points ignore n_sink / n_recent. */
+typedef struct {
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t page_size;
+  int32_t group_size;
+  int32_t n_sink;
+  int32_t n_recent;
+} kv4_layout;
+
+/* Cache storage (host struct of device pointers). */
+typedef struct {
+  void* pages;       /* [num_pages][num_kv_heads][block_bytes]          */
+  int64_t num_pages;
+  void* side;        /* [num_slots][num_kv_heads][kv4_side_bytes]; may be
+                        NULL when n_sink + n_recent == 0 or for kv8/kvbf16 */
+  int32_t num_slots;
+} kv4_cache;
+
+/* One batch of sequences (host struct of device pointers). */
+typedef struct {
+  const int32_t* page_table; /* [batch][max_pages] physical page ids       */
+  int32_t max_pages;         /* row stride of page_table; every sequence
+                                must satisfy seq_lens[b] <= 16 * max_pages */
+  const int32_t* seq_lens;   /* [batch] context length, counting the tokens
+                                appended by kv4_append in this step       */
+  const int32_t* slot_ids;   /* [batch] side-cache slot; NULL = slot b     */
+  int32_t batch;
+} kv4_batch;
+
+/* ---- versioning and status ------------------------------------------------ */
+int32_t kv4_abi_version(void);
+const char* kv4_status_string(kv4_status status); /* static string, never NULL */
+
+/* ---- sizes (host) ---------------------------------------------------------- */
+/* INT4 page block per (page, kv head), 18 * head_dim bytes (D = head_dim,
+ * r = position mod 16, c = channel, q4 = r/4, rr = r%4, t = c/16, n = c%16):
+ *   K codes  [0, 8D)    byte r*(D/2) + c/2, low nibble = even channel
+ *   V codes  [8D, 16D)  byte (q4*16 + n)*(D/8) + rr*(D/32) + t/2,
+ *                       low nibble = even t
+ *   K scales [16D, 17D) fp16 at byte (grp*16 + r)*2, grp = c/32
+ *   V scales [17D, 18D) fp16 likewise
+ * Nibbles are two's complement.  Returns 0 for an unsupported layout. */
+size_t kv4_block_bytes(const kv4_layout* layout);
+/* Side block per (slot, kv head): ceil((S+R)/16) INT8 tiles of 32*D + 64
+ * bytes; side row rho is row rho%16 of tile rho/16.  INT8 tile:
+ *   K codes  [0, 16D)      byte r*D + c
+ *   V codes  [16D, 32D)    byte (q4*16 + n)*(D/4) + t*4 + rr
+ *   K scales [32D, 32D+32) fp16 at 2r;  V scales [32D+32, 32D+64) fp16 at 2r */
+size_t kv4_side_bytes(const kv4_layout* layout);
+/* kv8 pages are single INT8 tiles (32*D + 64 bytes).  kvbf16 pages are 64*D
+ * bytes: K bf16 at element r*D + c; V at byte 32D + (q4*16 + n)*(D/2) +
+ * t*8 + rr*2. */
+size_t kv8_block_bytes(const kv4_layout* layout);
+size_t kvbf16_block_bytes(const kv4_layout* layout);
+
+/* ---- append ------------------------------------------------------------------
+ * Quantize and store new K/V tokens ([NEWS] Interpretation para 3: the whole
+ * context is kept in paged INT4; INT8 copies only for sinks and recent
+ * positions).  Sequence b receives n_b = cu_new[b+1] - cu_new[b] tokens at
+ * positions seq_lens[b] - n_b ... seq_lens[b] - 1; the caller has already
+ * added n_b to seq_lens[b] and mapped the pages of those positions in
+ * page_table.  Every new position is written to its INT4 page; a position
+ * p < S is also written to sink row p and a position p >= S (when R > 0) to
+ * ring row S + ((p - S) mod R) of side block slot_ids[b].
+ *   k_new, v_new  bf16 [total_new][num_kv_heads][head_dim]
+ *   cu_new        int32 [batch + 1], cu_new[0] = 0, non-decreasing,
+ *                 cu_new[batch] = total_new (device)
+ *   total_new     number of new tokens (host); 0 is a no-op
+ * Inputs must be finite.  Two positions of one call never share a byte, so
+ * any number of tokens per sequence may be appended in one call. */
+kv4_status kv4_append(const kv4_layout* layout, const kv4_cache* cache,
+                      const kv4_batch* batch, const uint16_t* k_new,
+                      const uint16_t* v_new, const int32_t* cu_new,
+                      int32_t total_new, hipStream_t stream);
+/* Same contract; INT8 pages (kv8) or bf16 pages (kvbf16); no side cache. */
+kv4_status kv8_append(const kv4_layout* layout, const kv4_cache* cache,
+                      const kv4_batch* batch, const uint16_t* k_new,
+                      const uint16_t* v_new, const int32_t* cu_new,
+                      int32_t total_new, hipStream_t stream);
+kv4_status kvbf16_append(const kv4_layout* layout, const kv4_cache* cache,
+                         const kv4_batch* batch, const uint16_t* k_new,
+                         const uint16_t* v_new, const int32_t* cu_new,
+                         int32_t total_new, hipStream_t stream);
+
+/* ---- decode ------------------------------------------------------------------
+ * Workspace needed by *_decode_attention for `batch` sequences with page
+ * tables of `max_pages` columns (host out-parameter). */
+kv4_status kv4_decode_workspace_size(const kv4_layout* layout, int32_t batch,
+                                     int32_t max_pages, size_t* bytes);
+
+/* Single-token GQA decode attention.  For sequence b and query head hq
+ * (kv head hq / (num_q_heads / num_kv_heads)) over the L = seq_lens[b]
+ * positions: sinks [0, min(S, L)) and recent [max(S, L-R), L) are read from
+ * the INT8 side cache, which replaces INT4 there; the middle [S, L-R) from the
+ * INT4 pages ([NEWS] Interpretation para 3; [ART]).  Scores are
+ * softmax_scale * q . k; the regions are combined by an exact log-sum-exp
+ * merge ([NEWS] Interpretation para 3), so the result equals one softmax over
+ * all positions of the dequantized keys.
+ *   q      bf16 [batch][num_q_heads][head_dim]
+ *   out    bf16 [batch][num_q_heads][head_dim] (rounded to nearest even)
+ *   lse    fp32 [batch][num_q_heads] natural-log sum of exp, or NULL
+ * L = 0 gives out = 0 and lse = -inf.  Arithmetic: exact dequantized
+ * products, fp32 accumulation.  The workspace is scratch for this call. */
+kv4_status kv4_decode_attention(const kv4_layout* layout, const kv4_cache* cache,
+                                const kv4_batch* batch, const uint16_t* q,
+                                float softmax_scale, uint16_t* out, float* lse,
+                                void* workspace, size_t workspace_bytes,
+                                hipStream_t stream);
+/* Reference variants at the same shapes: every position from INT8 pages
+ * (kv8) or bf16 pages (kvbf16) -- the KV8 and BF16 rollouts the pages compare
+ * against ([NEWS] Interpretation para 1). */
+kv4_status kv8_decode_attention(const kv4_layout* layout, const kv4_cache* cache,
+                                const kv4_batch* batch, const uint16_t* q,
+                                float softmax_scale, uint16_t* out, float* lse,
+                                void* workspace, size_t workspace_bytes,
+                                hipStream_t stream);
+kv4_status kvbf16_decode_attention(const kv4_layout* layout, const kv4_cache* cache,
+                                   const kv4_batch* batch, const uint16_t* q,
+                                   float softmax_scale, uint16_t* out, float* lse,
+                                   void* workspace, size_t workspace_bytes,
+                                   hipStream_t stream);
+
+/* ---- measurement aid ----------------------------------------------------------
+ * Streams `bytes` (a multiple of 16) of `buf` through 128-bit loads and
+ * stores one XOR-folded word per workgroup into `sink` (device,
+ * [kv4_probe_blocks] uint32) so the loads are not removed.  Used to measure
+ * the achievable HBM read bandwidth; not part of the decode path. */
+int32_t kv4_probe_blocks(void);
+kv4_status kv4_hbm_read_probe(const void* buf, size_t bytes, uint32_t* sink,
+                              hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KV4_H */

@@ -1,0 +1,197 @@
+// api.cpp -- the extern "C" boundary of libkv4: argument checks, sizes,
+// workspace carving and kernel launches.  Nothing here touches device memory.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "kv4.h"
+#include "kv4_common.h"
+#include "kv4_launch.h"
+
+namespace {
+
+using kv4::kFmtBF16;
+using kv4::kFmtKV4;
+using kv4::kFmtKV8;
+
+bool layout_valid(const kv4_layout* L) {
+  return L && L->num_kv_heads > 0 && L->num_q_heads > 0 && L->num_q_heads % L->num_kv_heads == 0 &&
+         L->n_sink >= 0 && L->n_recent >= 0;
+}
+
+kv4_status layout_check(const kv4_layout* L, int fmt) {
+  if (!layout_valid(L)) return KV4_ERR_INVALID_ARG;
+  if (L->head_dim != 64 && L->head_dim != 128) return KV4_ERR_UNSUPPORTED;
+  if (L->page_size != 16 || L->group_size != 32) return KV4_ERR_UNSUPPORTED;
+  const int g = L->num_q_heads / L->num_kv_heads;
+  if (g != 1 && g != 2 && g != 4 && g != 8) return KV4_ERR_UNSUPPORTED;
+  if (fmt == kFmtKV4 && L->n_sink + L->n_recent > kv4::kMaxProtected) return KV4_ERR_INVALID_ARG;
+  return KV4_OK;
+}
+
+size_t block_bytes(const kv4_layout* L, int fmt) {
+  if (!L || (L->head_dim != 64 && L->head_dim != 128)) return 0;
+  const int D = L->head_dim;
+  if (fmt == kFmtKV4) return kv4::int4_block_bytes(D);
+  if (fmt == kFmtKV8) return kv4::int8_tile_bytes(D);
+  return kv4::bf16_tile_bytes(D);
+}
+
+size_t side_bytes(const kv4_layout* L) {
+  if (!L || (L->head_dim != 64 && L->head_dim != 128) || L->n_sink < 0 || L->n_recent < 0) return 0;
+  return size_t(kv4::side_tiles(L->n_sink, L->n_recent)) * kv4::int8_tile_bytes(L->head_dim);
+}
+
+bool protected_set(const kv4_layout* L, int fmt) { return fmt == kFmtKV4 && L->n_sink + L->n_recent > 0; }
+
+kv4_status cache_batch_check(const kv4_layout* L, const kv4_cache* c, const kv4_batch* b, int fmt) {
+  if (!c || !b) return KV4_ERR_INVALID_ARG;
+  if (!c->pages || c->num_pages <= 0) return KV4_ERR_INVALID_ARG;
+  if (b->batch < 0 || b->max_pages <= 0) return KV4_ERR_INVALID_ARG;
+  if (b->batch > 0 && (!b->page_table || !b->seq_lens)) return KV4_ERR_INVALID_ARG;
+  if (protected_set(L, fmt) && (!c->side || c->num_slots <= 0)) return KV4_ERR_INVALID_ARG;
+  return KV4_OK;
+}
+
+kv4_status append_impl(int fmt, const kv4_layout* L, const kv4_cache* c, const kv4_batch* b,
+                       const uint16_t* k, const uint16_t* v, const int32_t* cu, int32_t total,
+                       hipStream_t stream) {
+  kv4_status s = layout_check(L, fmt);
+  if (s != KV4_OK) return s;
+  s = cache_batch_check(L, c, b, fmt);
+  if (s != KV4_OK) return s;
+  if (total < 0) return KV4_ERR_INVALID_ARG;
+  if (total == 0 || b->batch == 0) return KV4_OK;
+  if (!k || !v || !cu) return KV4_ERR_INVALID_ARG;
+  kv4::AppendParams p{};
+  p.pages = static_cast<uint8_t*>(c->pages);
+  p.num_pages = c->num_pages;
+  p.side = static_cast<uint8_t*>(c->side);
+  p.num_slots = c->num_slots;
+  p.page_table = b->page_table;
+  p.max_pages = b->max_pages;
+  p.seq_lens = b->seq_lens;
+  p.slot_ids = b->slot_ids;
+  p.batch = b->batch;
+  p.k_new = k;
+  p.v_new = v;
+  p.cu_new = cu;
+  p.total_new = total;
+  p.num_kv_heads = L->num_kv_heads;
+  p.n_sink = fmt == kFmtKV4 ? L->n_sink : 0;
+  p.n_recent = fmt == kFmtKV4 ? L->n_recent : 0;
+  p.block_bytes = int64_t(block_bytes(L, fmt));
+  p.side_bytes = int64_t(side_bytes(L));
+  if (!protected_set(L, fmt)) {
+    p.side = nullptr;
+    p.num_slots = 0;
+  }
+  return kv4::launch_append(fmt, p, L->head_dim, stream) == hipSuccess ? KV4_OK : KV4_ERR_LAUNCH;
+}
+
+kv4_status decode_impl(int fmt, const kv4_layout* L, const kv4_cache* c, const kv4_batch* b,
+                       const uint16_t* q, float sm, uint16_t* out, float* lse, void* ws, size_t ws_bytes,
+                       hipStream_t stream) {
+  kv4_status s = layout_check(L, fmt);
+  if (s != KV4_OK) return s;
+  s = cache_batch_check(L, c, b, fmt);
+  if (s != KV4_OK) return s;
+  if (b->batch == 0) return KV4_OK;
+  if (!q || !out || !ws) return KV4_ERR_INVALID_ARG;
+  const size_t need = kv4::decode_workspace_bytes(b->batch, b->max_pages, L->num_q_heads, L->head_dim);
+  if (ws_bytes < need) return KV4_ERR_WORKSPACE;
+  kv4::DecodeParams p{};
+  p.pages = static_cast<const uint8_t*>(c->pages);
+  p.num_pages = c->num_pages;
+  p.side = static_cast<const uint8_t*>(c->side);
+  p.num_slots = c->num_slots;
+  p.page_table = b->page_table;
+  p.max_pages = b->max_pages;
+  p.seq_lens = b->seq_lens;
+  p.slot_ids = b->slot_ids;
+  p.batch = b->batch;
+  p.q = q;
+  p.softmax_scale = sm;
+  p.out = out;
+  p.lse = lse;
+  p.num_q_heads = L->num_q_heads;
+  p.num_kv_heads = L->num_kv_heads;
+  p.n_sink = fmt == kFmtKV4 ? L->n_sink : 0;
+  p.n_recent = fmt == kFmtKV4 ? L->n_recent : 0;
+  p.block_bytes = int64_t(block_bytes(L, fmt));
+  p.side_bytes = int64_t(side_bytes(L));
+  p.chunk_pages = kv4::decode_chunk_pages();
+  p.ws = kv4::carve_workspace(ws, b->batch, b->max_pages, L->num_q_heads, L->head_dim);
+  if (!protected_set(L, fmt)) {
+    p.side = nullptr;
+    p.num_slots = 0;
+  }
+  return kv4::launch_decode(fmt, p, L->head_dim, stream) == hipSuccess ? KV4_OK : KV4_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t kv4_abi_version(void) { return KV4_ABI_VERSION; }
+
+const char* kv4_status_string(kv4_status s) {
+  switch (s) {
+    case KV4_OK: return "ok";
+    case KV4_ERR_INVALID_ARG: return "invalid argument";
+    case KV4_ERR_UNSUPPORTED: return "unsupported shape";
+    case KV4_ERR_WORKSPACE: return "workspace too small";
+    case KV4_ERR_LAUNCH: return "kernel launch failed";
+  }
+  return "unknown status";
+}
+
+size_t kv4_block_bytes(const kv4_layout* L) { return block_bytes(L, kFmtKV4); }
+size_t kv8_block_bytes(const kv4_layout* L) { return block_bytes(L, kFmtKV8); }
+size_t kvbf16_block_bytes(const kv4_layout* L) { return block_bytes(L, kFmtBF16); }
+size_t kv4_side_bytes(const kv4_layout* L) { return side_bytes(L); }
+
+kv4_status kv4_append(const kv4_layout* L, const kv4_cache* c, const kv4_batch* b, const uint16_t* k,
+                      const uint16_t* v, const int32_t* cu, int32_t total, hipStream_t stream) {
+  return append_impl(kFmtKV4, L, c, b, k, v, cu, total, stream);
+}
+kv4_status kv8_append(const kv4_layout* L, const kv4_cache* c, const kv4_batch* b, const uint16_t* k,
+                      const uint16_t* v, const int32_t* cu, int32_t total, hipStream_t stream) {
+  return append_impl(kFmtKV8, L, c, b, k, v, cu, total, stream);
+}
+kv4_status kvbf16_append(const kv4_layout* L, const kv4_cache* c, const kv4_batch* b, const uint16_t* k,
+                         const uint16_t* v, const int32_t* cu, int32_t total, hipStream_t stream) {
+  return append_impl(kFmtBF16, L, c, b, k, v, cu, total, stream);
+}
+
+kv4_status kv4_decode_workspace_size(const kv4_layout* L, int32_t batch, int32_t max_pages, size_t* bytes) {
+  if (!layout_valid(L) || !bytes || batch < 0 || max_pages <= 0) return KV4_ERR_INVALID_ARG;
+  if (L->head_dim != 64 && L->head_dim != 128) return KV4_ERR_UNSUPPORTED;
+  *bytes = kv4::decode_workspace_bytes(batch, max_pages, L->num_q_heads, L->head_dim);
+  return KV4_OK;
+}
+
+kv4_status kv4_decode_attention(const kv4_layout* L, const kv4_cache* c, const kv4_batch* b, const uint16_t* q,
+                                float sm, uint16_t* out, float* lse, void* ws, size_t ws_bytes,
+                                hipStream_t stream) {
+  return decode_impl(kFmtKV4, L, c, b, q, sm, out, lse, ws, ws_bytes, stream);
+}
+kv4_status kv8_decode_attention(const kv4_layout* L, const kv4_cache* c, const kv4_batch* b, const uint16_t* q,
+                                float sm, uint16_t* out, float* lse, void* ws, size_t ws_bytes,
+                                hipStream_t stream) {
+  return decode_impl(kFmtKV8, L, c, b, q, sm, out, lse, ws, ws_bytes, stream);
+}
+kv4_status kvbf16_decode_attention(const kv4_layout* L, const kv4_cache* c, const kv4_batch* b,
+                                   const uint16_t* q, float sm, uint16_t* out, float* lse, void* ws,
+                                   size_t ws_bytes, hipStream_t stream) {
+  return decode_impl(kFmtBF16, L, c, b, q, sm, out, lse, ws, ws_bytes, stream);
+}
+
+int32_t kv4_probe_blocks(void) { return kv4::probe_blocks(); }
+
+kv4_status kv4_hbm_read_probe(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream) {
+  if (!buf || !sink || bytes == 0 || bytes % 16) return KV4_ERR_INVALID_ARG;
+  return kv4::launch_probe(buf, bytes, sink, stream) == hipSuccess ? KV4_OK : KV4_ERR_LAUNCH;
+}
+
+}  // extern "C"

@@ -1,0 +1,76 @@
+// kv4_launch.h -- kernel parameter blocks and launchers (host side of libkv4).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kv4 {
+
+struct AppendParams {
+  uint8_t* pages;
+  int64_t num_pages;
+  uint8_t* side;
+  int32_t num_slots;
+  const int32_t* page_table;
+  int32_t max_pages;
+  const int32_t* seq_lens;
+  const int32_t* slot_ids;
+  int32_t batch;
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  const int32_t* cu_new;
+  int32_t total_new;
+  int32_t num_kv_heads;
+  int32_t n_sink;
+  int32_t n_recent;
+  int64_t block_bytes;
+  int64_t side_bytes;
+};
+
+hipError_t launch_append(int fmt, const AppendParams& p, int head_dim, hipStream_t stream);
+
+// Decode workspace: a header, the per-sequence item table, the work items and
+// the fp32 partial results of sequences split over several items.
+struct DecodeWorkspace {
+  uint32_t* header;      // [0] unit counter, [1] total items
+  int32_t* item_base;    // [batch]
+  int32_t* item_count;   // [batch]
+  int2* items;           // [max_items] (sequence, chunk)
+  float* partials;       // [max_items][num_q_heads][head_dim + 2]
+  int64_t max_items;
+};
+
+struct DecodeParams {
+  const uint8_t* pages;
+  int64_t num_pages;
+  const uint8_t* side;
+  int32_t num_slots;
+  const int32_t* page_table;
+  int32_t max_pages;
+  const int32_t* seq_lens;
+  const int32_t* slot_ids;
+  int32_t batch;
+  const uint16_t* q;
+  float softmax_scale;
+  uint16_t* out;
+  float* lse;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t n_sink;
+  int32_t n_recent;
+  int64_t block_bytes;
+  int64_t side_bytes;
+  int32_t chunk_pages;
+  DecodeWorkspace ws;
+};
+
+int32_t decode_chunk_pages();
+size_t decode_workspace_bytes(int32_t batch, int32_t max_pages, int32_t num_q_heads, int32_t head_dim);
+DecodeWorkspace carve_workspace(void* base, int32_t batch, int32_t max_pages, int32_t num_q_heads,
+                                int32_t head_dim);
+hipError_t launch_decode(int fmt, const DecodeParams& p, int head_dim, hipStream_t stream);
+
+hipError_t launch_probe(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream);
+int32_t probe_blocks();
+
+}  // namespace kv4

@@ -1,0 +1,120 @@
+"""The C-ABI library loads, exports every declared symbol and rejects bad
+arguments on the host before launching anything (runs without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import int4_kv_cache_amd as kv4
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kv4.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\**\s+\**([a-z][a-z0-9_]*)\s*\(",
+                       src, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(kv4.LIB_PATH):
+        pytest.fail("libkv4.so is not built (python -m int4_kv_cache_amd.build)")
+    return kv4.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) >= 15, names
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in kv4.h but not exported"
+    assert set(names) == set(kv4.EXPORTS)
+
+
+def test_version_and_status_strings(lib):
+    assert lib.kv4_abi_version() == 1
+    for code, text in kv4.STATUS.items():
+        assert lib.kv4_status_string(code).decode() == text
+    assert lib.kv4_status_string(12345).decode() == "unknown status"
+
+
+def test_sizes_closed_form(lib):
+    for D in (64, 128):
+        lay = kv4.make_layout(32, 8, D, 16, 128)
+        assert kv4.block_bytes(kv4.FMT_KV4, lay) == 18 * D
+        assert kv4.block_bytes(kv4.FMT_KV8, lay) == 32 * D + 64
+        assert kv4.block_bytes(kv4.FMT_BF16, lay) == 64 * D
+        assert kv4.side_bytes(lay) == 9 * (32 * D + 64)
+    assert kv4.side_bytes(kv4.make_layout(32, 8, 128, 0, 0)) == 0
+    assert kv4.block_bytes(kv4.FMT_KV4, kv4.make_layout(32, 8, 96, 0, 0)) == 0
+
+
+def test_workspace_size(lib):
+    lay = kv4.make_layout(32, 8, 128, 16, 128)
+    a = kv4.workspace_bytes(lay, 1024, 1040)
+    b = kv4.workspace_bytes(lay, 1024, 2080)
+    assert 0 < a < b
+    with pytest.raises(kv4.Kv4Error) as e:
+        kv4.workspace_bytes(lay, 1024, 0)
+    assert e.value.status == -1
+    with pytest.raises(kv4.Kv4Error) as e:
+        kv4.workspace_bytes(kv4.make_layout(32, 8, 96, 0, 0), 4, 4)
+    assert e.value.status == -2
+
+
+def _call_decode(lib, lay, cache, batch, q=1, out=1, ws=1, ws_bytes=1 << 40):
+    return lib.kv4_decode_attention(ctypes.byref(lay), ctypes.byref(cache) if cache else None,
+                                    ctypes.byref(batch) if batch else None, q, 1.0, out, None, ws,
+                                    ws_bytes, None)
+
+
+def test_host_argument_errors_return_before_launch(lib):
+    """Fake (never dereferenced) pointers: each call must fail on the host."""
+    good = kv4.make_layout(32, 8, 128, 16, 128)
+    fake = 0x1000
+    cache = kv4.CacheDesc(fake, 10, fake, 4)
+    batch = kv4.BatchDesc(fake, 4, fake, None, 4)
+    # bad layouts
+    for lay, want in [(kv4.make_layout(32, 7, 128, 16, 128), -1),    # Hq % Hkv
+                      (kv4.make_layout(32, 8, 96, 16, 128), -2),     # head_dim
+                      (kv4.make_layout(32, 8, 128, 16, 129), -1),    # S + R > 144
+                      (kv4.make_layout(32, 8, 128, -1, 0), -1),
+                      (kv4.make_layout(32, 8, 128, 16, 128, page_size=32), -2),
+                      (kv4.make_layout(32, 8, 128, 16, 128, group_size=64), -2),
+                      (kv4.make_layout(48, 8, 128, 16, 128), -2)]:  # g = 6
+        assert _call_decode(lib, lay, cache, batch) == want
+        assert lib.kv4_append(ctypes.byref(lay), ctypes.byref(cache), ctypes.byref(batch),
+                              fake, fake, fake, 3, None) == want
+    # null structs / pointers
+    assert _call_decode(lib, good, None, batch) == -1
+    assert _call_decode(lib, good, cache, None) == -1
+    assert _call_decode(lib, good, cache, batch, q=None) == -1
+    assert _call_decode(lib, good, cache, batch, out=None) == -1
+    assert _call_decode(lib, good, cache, batch, ws=None) == -1
+    assert _call_decode(lib, good, kv4.CacheDesc(fake, 10, None, 0), batch) == -1   # side needed
+    assert _call_decode(lib, good, kv4.CacheDesc(None, 10, fake, 4), batch) == -1
+    assert _call_decode(lib, good, cache, kv4.BatchDesc(None, 4, fake, None, 4)) == -1
+    assert _call_decode(lib, good, cache, kv4.BatchDesc(fake, 0, fake, None, 4)) == -1
+    # workspace too small
+    assert _call_decode(lib, good, cache, batch, ws_bytes=16) == -3
+    # append argument errors
+    assert lib.kv4_append(ctypes.byref(good), ctypes.byref(cache), ctypes.byref(batch), fake, fake,
+                          fake, -1, None) == -1
+    assert lib.kv4_append(ctypes.byref(good), ctypes.byref(cache), ctypes.byref(batch), None, fake,
+                          fake, 3, None) == -1
+    # zero work is a no-op and succeeds without launching
+    assert lib.kv4_append(ctypes.byref(good), ctypes.byref(cache), ctypes.byref(batch), None, None,
+                          None, 0, None) == 0
+    assert _call_decode(lib, good, cache, kv4.BatchDesc(fake, 4, fake, None, 0)) == 0
+    # plain INT4 needs no side cache; kv8 / kvbf16 ignore it
+    plain = kv4.make_layout(32, 8, 128, 0, 0)
+    assert _call_decode(lib, plain, kv4.CacheDesc(fake, 10, None, 0), batch, ws_bytes=16) == -3
+    assert lib.kv8_decode_attention(ctypes.byref(good), ctypes.byref(kv4.CacheDesc(fake, 10, None, 0)),
+                                    ctypes.byref(batch), fake, 1.0, fake, None, fake, 16, None) == -3
+    # probe
+    assert lib.kv4_hbm_read_probe(fake, 17, fake, None) == -1
+    assert lib.kv4_hbm_read_probe(None, 16, fake, None) == -1
