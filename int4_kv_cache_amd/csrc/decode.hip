@@ -1,39 +1,404 @@
-// decode.hip -- single-token GQA decode attention over the paged caches.
+// decode.hip -- single-token GQA decode attention over the paged caches,
+// with QK^T and PV on the gfx950 matrix cores (v_mfma_f32_16x16x32_bf16).
 //
 // Three kernels on the caller's stream:
 //   1. worklist  (1 workgroup): per sequence, the number of work items.  The
-//      middle region is cut into chunks of `chunk_pages` INT4 pages; item 0
-//      also carries the protected rows (INT8 sinks + recent ring).
-//   2. attention (persistent grid, one wave per unit = item x kv head): the
-//      online softmax over the item's rows.  A sequence with one item writes
-//      the final bf16 output and lse directly; otherwise the item writes an
-//      fp32 partial (o, m, l).
+//      middle region is cut into chunks of kChunkPages pages; item 0 also
+//      carries the protected rows (INT8 sinks + recent ring).
+//   2. attention (persistent grid; one wave per unit = item x kv head x head
+//      block): online softmax over the item's 16-row tiles, two tiles (32
+//      positions) per step.  A sequence with one item writes the bf16 output
+//      and lse directly, otherwise an fp32 partial (o, m, l).
 //   3. merge: exact log-sum-exp merge of the partials of split sequences.
-// The regional merge is exact (news summary "Async RL squeezes context into
-// fewer decode steps; ...", Interpretation paragraph 3): processing protected
-// and middle rows in one online softmax, or in several partials merged by
-// log-sum-exp, both equal one softmax over all positions.
+// Processing sinks, middle and recent rows in one online softmax, or in
+// partials merged by log-sum-exp, both equal one softmax over all positions:
+// the exact regional merge of the news summary "Async RL squeezes context
+// into fewer decode steps; ...", Interpretation paragraph 3.
+//
+// Matrix-core mapping (rows m = (head, 32-channel group): 4 heads x 4 groups
+// at head_dim 128, 8 x 2 at 64):
+//   QK  A = 16 positions x 32 channels of K codes, B = q with row m holding
+//       only its own group's channels, so D[pos][m] is the per-group partial
+//       dot product; the per-(position, group) INT4 scale is applied after.
+//   PV  A = p * v_scale for row m (its group's scale), K = 32 positions,
+//       B = V codes of 16 channels; row m is used only for channels of its
+//       group.  p is split into bf16 hi + lo so the product keeps ~16 bits.
+// INT4 codes enter the MFMA as the exact bf16 value 1 + (code + 8)/16 (two
+// bit operations per pair of codes); the constant part is removed through
+// the accumulator input (-1.5 * sum of the other operand), which leaves
+// sum(x * code) / 16 exactly up to fp32 rounding.
 #include "kv4_common.h"
 #include "kv4_launch.h"
 
 namespace kv4 {
 namespace {
 
-constexpr int kChunkPages = 32;
+typedef __bf16 bf16x8_t __attribute__((__vector_size__(16)));
+typedef float f32x4_t __attribute__((__vector_size__(16)));
+typedef uint32_t u32x4_t __attribute__((__vector_size__(16)));
+
+constexpr int kChunkPages = 32;  // middle pages per work item (<= 64)
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kRescale = 8.0f;  // re-reference the running max when it grows by 2^8
+
+enum Kind : int { kInt4Page = 0, kInt8Tile = 1, kBf16Page = 2 };
+
+__device__ inline bf16x8_t bf8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  u32x4_t v = {a, b, c, d};
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+__device__ inline f32x4_t mfma(bf16x8_t a, bf16x8_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+// two fp32 -> packed bf16 pair, round to nearest even
+__device__ inline uint32_t pack_bf16(float lo, float hi) {
+  typedef __bf16 bf16x2_t __attribute__((__vector_size__(4)));
+  bf16x2_t v;
+  v[0] = __bf16(lo);
+  v[1] = __bf16(hi);
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+// two small exact integers in fp32 -> bf16 pair (the low halves are zero)
+__device__ inline uint32_t pack_exact(float lo, float hi) {
+  return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+}
+__device__ inline float h2f_lo(uint32_t w) { return f16_to_f32(uint16_t(w & 0xFFFF)); }
+__device__ inline float h2f_hi(uint32_t w) { return f16_to_f32(uint16_t(w >> 16)); }
+__device__ inline float sbyte(uint32_t w, int k) { return float(int32_t(w << (24 - 8 * k)) >> 24); }
+
+// INT4: nibbles k and k+4 of d -> bf16 pair 1 + (code+8)/16.
+template <int K>
+__device__ inline uint32_t nib_pair(uint32_t d) {
+  const uint32_t x = K == 0 ? (d << 3) : (d >> (4 * K - 3));
+  return (x & 0x00780078u) ^ 0x3FC03FC0u;
+}
+// INT4 V: x holds one byte at bits 0-7 and one at 16-23; take the low (HIGH
+// = false) or high nibble of each as a bf16 pair 1 + (code+8)/16.
+template <bool HIGH>
+__device__ inline uint32_t vnib_pair(uint32_t x) {
+  const uint32_t y = HIGH ? (x >> 1) : (x << 3);
+  return (y & 0x00780078u) ^ 0x3FC03FC0u;
+}
+
+// ------------------------------------------------------------ tile loads --
+template <int KIND, int D>
+struct Tile;
+
+template <int D>
+struct Tile<kInt4Page, D> {
+  static constexpr int KW = D / 32;  // dwords of K codes per lane (D/8 bytes)
+  uint32_t k[KW];
+  uint32_t v[KW];
+  uint32_t ks[2], vs[2];  // fp16 scales of positions 4kg..4kg+3, group = ln % NG
+  __device__ inline void load(const uint8_t* __restrict__ blk, int ln, int kg) {
+    constexpr int NG = D / 32;
+    const int grp = ln % NG;
+    const uint8_t* kp = blk + ln * (D / 2) + kg * (D / 8);
+    const uint8_t* vp = blk + 8 * D + (kg * 16 + ln) * (D / 8);
+    if constexpr (KW == 4) {
+      const uint4 a = *reinterpret_cast<const uint4*>(kp);
+      const uint4 b = *reinterpret_cast<const uint4*>(vp);
+      k[0] = a.x; k[1] = a.y; k[2] = a.z; k[3] = a.w;
+      v[0] = b.x; v[1] = b.y; v[2] = b.z; v[3] = b.w;
+    } else {
+      const uint2 a = *reinterpret_cast<const uint2*>(kp);
+      const uint2 b = *reinterpret_cast<const uint2*>(vp);
+      k[0] = a.x; k[1] = a.y;
+      v[0] = b.x; v[1] = b.y;
+    }
+    const uint2 s = *reinterpret_cast<const uint2*>(blk + 16 * D + (grp * 16 + kg * 4) * 2);
+    const uint2 t = *reinterpret_cast<const uint2*>(blk + 17 * D + (grp * 16 + kg * 4) * 2);
+    ks[0] = s.x; ks[1] = s.y;
+    vs[0] = t.x; vs[1] = t.y;
+  }
+};
+
+template <int D>
+struct Tile<kInt8Tile, D> {
+  static constexpr int KW = D / 16;  // D/4 bytes per lane
+  uint32_t k[KW];
+  uint32_t v[KW];
+  uint32_t ks[2], vs[2];
+  __device__ inline void load(const uint8_t* __restrict__ tile, int ln, int kg) {
+    const uint8_t* kp = tile + ln * D + kg * (D / 4);
+    const uint8_t* vp = tile + 16 * D + (kg * 16 + ln) * (D / 4);
+#pragma unroll
+    for (int i = 0; i < KW / 4; ++i) {
+      const uint4 a = reinterpret_cast<const uint4*>(kp)[i];
+      const uint4 b = reinterpret_cast<const uint4*>(vp)[i];
+      k[4 * i] = a.x; k[4 * i + 1] = a.y; k[4 * i + 2] = a.z; k[4 * i + 3] = a.w;
+      v[4 * i] = b.x; v[4 * i + 1] = b.y; v[4 * i + 2] = b.z; v[4 * i + 3] = b.w;
+    }
+    const uint2 s = *reinterpret_cast<const uint2*>(tile + 32 * D + kg * 8);
+    const uint2 t = *reinterpret_cast<const uint2*>(tile + 32 * D + 32 + kg * 8);
+    ks[0] = s.x; ks[1] = s.y;
+    vs[0] = t.x; vs[1] = t.y;
+  }
+};
+
+template <int D>
+struct Tile<kBf16Page, D> {
+  static constexpr int KW = D / 8;  // D/2 bytes per lane
+  uint32_t k[KW];
+  uint32_t v[KW];
+  __device__ inline void load(const uint8_t* __restrict__ tile, int ln, int kg) {
+    const uint8_t* kp = tile + (ln * D + kg * (D / 4)) * 2;
+    const uint8_t* vp = tile + 32 * D + (kg * 16 + ln) * (D / 2);
+#pragma unroll
+    for (int i = 0; i < KW / 4; ++i) {
+      const uint4 a = reinterpret_cast<const uint4*>(kp)[i];
+      const uint4 b = reinterpret_cast<const uint4*>(vp)[i];
+      k[4 * i] = a.x; k[4 * i + 1] = a.y; k[4 * i + 2] = a.z; k[4 * i + 3] = a.w;
+      v[4 * i] = b.x; v[4 * i + 1] = b.y; v[4 * i + 2] = b.z; v[4 * i + 3] = b.w;
+    }
+  }
+};
+
+// ----------------------------------------------------------- unit state --
+template <int D>
+struct Unit {
+  static constexpr int NG = D / 32;  // scale groups per head
+  static constexpr int NT = D / 16;  // PV N-tiles
+  bf16x8_t bq[NG];                   // q operand per QK MFMA
+  float qsum;                        // sum of this lane's row (head, group) of q
+  f32x4_t o[NT];                     // PV accumulators (D layout)
+  float m;                           // running max (log2 units) of head ln / NG
+  float l;                           // this lane's share of the softmax denominator
+  float qk_scale;                    // softmax_scale * log2(e)
+};
+
+// QK for one tile -> x[e] = scaled per-group partial score of position 4kg+e.
+template <int KIND, int D>
+__device__ inline void qk_tile(const Unit<D>& u, const Tile<KIND, D>& T, float (&x)[4]) {
+  constexpr int NG = D / 32;
+  f32x4_t acc;
+  if constexpr (KIND == kInt4Page) {
+    const float c = -1.5f * u.qsum;
+    acc = f32x4_t{c, c, c, c};
+#pragma unroll
+    for (int t = 0; t < NG; ++t) {
+      const uint32_t d = T.k[t];
+      acc = mfma(bf8(nib_pair<0>(d), nib_pair<1>(d), nib_pair<2>(d), nib_pair<3>(d)), u.bq[t], acc);
+    }
+  } else if constexpr (KIND == kInt8Tile) {
+    acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < NG; ++t) {
+      const uint32_t w0 = T.k[2 * t], w1 = T.k[2 * t + 1];
+      acc = mfma(bf8(pack_exact(sbyte(w0, 0), sbyte(w1, 0)), pack_exact(sbyte(w0, 1), sbyte(w1, 1)),
+                     pack_exact(sbyte(w0, 2), sbyte(w1, 2)), pack_exact(sbyte(w0, 3), sbyte(w1, 3))),
+                 u.bq[t], acc);
+    }
+  } else {
+    acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < NG; ++t)
+      acc = mfma(bf8(T.k[4 * t], T.k[4 * t + 1], T.k[4 * t + 2], T.k[4 * t + 3]), u.bq[t], acc);
+  }
+  if constexpr (KIND == kBf16Page) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] = acc[e] * u.qk_scale;
+  } else {
+    const float s = KIND == kInt4Page ? 16.0f * u.qk_scale : u.qk_scale;
+    x[0] = acc[0] * h2f_lo(T.ks[0]) * s;
+    x[1] = acc[1] * h2f_hi(T.ks[0]) * s;
+    x[2] = acc[2] * h2f_lo(T.ks[1]) * s;
+    x[3] = acc[3] * h2f_hi(T.ks[1]) * s;
+  }
+}
+
+
+// Zero mask of the two bf16 halves of a position pair: a half is cleared when
+// its position is not part of the context (bf16 pages only: unused rows may
+// hold any bit pattern, and 0 * NaN would poison the accumulator).
+__device__ inline uint32_t pair_zero_mask(uint32_t valid4, int r) {
+  return (((valid4 >> r) & 1u) ? 0u : 0x0000FFFFu) | (((valid4 >> (r + 1)) & 1u) ? 0u : 0xFFFF0000u);
+}
+
+// V operand of PV N-tile t from two tiles: positions 4kg..4kg+3 of T0 then of
+// T1, channel 16t + ln.  valid0/valid1: the lane's 4 position bits per tile.
+template <int KIND, int D>
+__device__ inline bf16x8_t v_operand(const Tile<KIND, D>& T0, const Tile<KIND, D>& T1, int t,
+                                     uint32_t valid0, uint32_t valid1) {
+  if constexpr (KIND == kInt4Page) {
+    // position rr's D/32 bytes start at byte rr*(D/32); channel 16t+n is
+    // nibble t of them: byte t/2, low nibble for even t.
+    constexpr int PB = D / 32;
+    auto pair = [&](const Tile<KIND, D>& T, int r0) -> uint32_t {
+      const int o0 = r0 * PB + t / 2, o1 = (r0 + 1) * PB + t / 2;
+      const uint32_t a = T.v[o0 >> 2], b = T.v[o1 >> 2];
+      const uint32_t sel = uint32_t(o0 & 3) | (0x0Cu << 8) | (uint32_t(4 + (o1 & 3)) << 16) | (0x0Cu << 24);
+      const uint32_t x = __builtin_amdgcn_perm(b, a, sel);
+      return (t & 1) ? vnib_pair<true>(x) : vnib_pair<false>(x);
+    };
+    return bf8(pair(T0, 0), pair(T0, 2), pair(T1, 0), pair(T1, 2));
+  } else if constexpr (KIND == kInt8Tile) {
+    const uint32_t a = T0.v[t], b = T1.v[t];
+    return bf8(pack_exact(sbyte(a, 0), sbyte(a, 1)), pack_exact(sbyte(a, 2), sbyte(a, 3)),
+               pack_exact(sbyte(b, 0), sbyte(b, 1)), pack_exact(sbyte(b, 2), sbyte(b, 3)));
+  } else {
+    return bf8(T0.v[2 * t] & ~pair_zero_mask(valid0, 0), T0.v[2 * t + 1] & ~pair_zero_mask(valid0, 2),
+               T1.v[2 * t] & ~pair_zero_mask(valid1, 0), T1.v[2 * t + 1] & ~pair_zero_mask(valid1, 2));
+  }
+}
+
+// Per-head value (held by score-layout lane head*NG) for the PV-layout
+// accumulator element e of this lane.
+template <int D>
+__device__ inline float head_value_for_acc(float v, int lane, int e) {
+  constexpr int NG = D / 32;
+  if constexpr (NG == 4) {
+    return __shfl(v, (lane >> 4) * 4, kWave);
+  } else {
+    return __shfl(v, ((lane >> 4) * 2 + (e >> 1)) * 2, kWave);
+  }
+}
+
+// One step: two 16-row tiles (32 positions).  mask0/mask1: 16-bit row masks.
+template <int KIND, int D>
+__device__ inline void step(Unit<D>& u, const Tile<KIND, D>& T0, const Tile<KIND, D>& T1, uint32_t mask0,
+                            uint32_t mask1, int lane) {
+  constexpr int NG = D / 32;
+  constexpr int NT = D / 16;
+  const int kg = lane >> 4;
+  const uint32_t va0 = (mask0 >> (4 * kg)) & 15u, va1 = (mask1 >> (4 * kg)) & 15u;
+
+  float x0[4], x1[4];
+  qk_tile<KIND, D>(u, T0, x0);
+  qk_tile<KIND, D>(u, T1, x1);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    x0[e] += __shfl_xor(x0[e], 1, kWave);
+    x1[e] += __shfl_xor(x1[e], 1, kWave);
+    if constexpr (NG == 4) {
+      x0[e] += __shfl_xor(x0[e], 2, kWave);
+      x1[e] += __shfl_xor(x1[e], 2, kWave);
+    }
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    x0[e] = ((va0 >> e) & 1u) ? x0[e] : -INFINITY;
+    x1[e] = ((va1 >> e) & 1u) ? x1[e] : -INFINITY;
+    mx = fmaxf(mx, fmaxf(x0[e], x1[e]));
+  }
+  mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+  mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+
+  // Re-reference the running max only when it grew by 2^kRescale: p stays
+  // below 2^8, and the accumulators are rescaled rarely.
+  const bool need = mx > u.m + kRescale;
+  if (__any(need)) {
+    const float mn = fmaxf(u.m, mx);
+    const float alpha = (mn == u.m) ? 1.0f : exp2f(u.m - mn);
+    u.l *= alpha;
+    u.m = mn;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int e0 = t / 2;
+      u.o[t][e0] *= head_value_for_acc<D>(alpha, lane, e0);
+      if constexpr (NG == 2) u.o[t][e0 + 2] *= head_value_for_acc<D>(alpha, lane, e0 + 2);
+    }
+  }
+
+  float pr[8];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    pr[e] = ((va0 >> e) & 1u) ? exp2f(x0[e] - u.m) : 0.f;
+    pr[e + 4] = ((va1 >> e) & 1u) ? exp2f(x1[e] - u.m) : 0.f;
+  }
+  u.l += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
+
+  // A operand of PV: p * v_scale of (position, this row's group), split into
+  // bf16 hi + lo.  Rows outside the context contribute exactly 0.
+  float ap[8];
+  if constexpr (KIND == kBf16Page) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ap[e] = pr[e] * 0.0625f;
+  } else {
+    const float sc = KIND == kInt4Page ? 1.0f : 0.0625f;
+    const float sv[8] = {h2f_lo(T0.vs[0]), h2f_hi(T0.vs[0]), h2f_lo(T0.vs[1]), h2f_hi(T0.vs[1]),
+                         h2f_lo(T1.vs[0]), h2f_hi(T1.vs[0]), h2f_lo(T1.vs[1]), h2f_hi(T1.vs[1])};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      ap[e] = ((va0 >> e) & 1u) ? pr[e] * sv[e] * sc : 0.f;
+      ap[e + 4] = ((va1 >> e) & 1u) ? pr[e + 4] * sv[e + 4] * sc : 0.f;
+    }
+  }
+  uint32_t hi[4], lo[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    hi[j] = pack_bf16(ap[2 * j], ap[2 * j + 1]);
+    lo[j] = pack_bf16(ap[2 * j] - bf16_lo(hi[j]), ap[2 * j + 1] - bf16_hi(hi[j]));
+  }
+  const bf16x8_t a_hi = bf8(hi[0], hi[1], hi[2], hi[3]);
+  const bf16x8_t a_lo = bf8(lo[0], lo[1], lo[2], lo[3]);
+
+  f32x4_t corr = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (KIND == kInt4Page) {
+    // -1.5 * sum over the 32 positions of this row's A: removes the constant
+    // part of the 1 + (code+8)/16 encoding of the V codes.
+    const bf16x8_t ones = bf8(0xBFC0BFC0u, 0xBFC0BFC0u, 0xBFC0BFC0u, 0xBFC0BFC0u);
+    corr = mfma(a_hi, ones, corr);
+    corr = mfma(a_lo, ones, corr);
+  }
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const bf16x8_t bv = v_operand<KIND, D>(T0, T1, t, va0, va1);
+    f32x4_t c = u.o[t];
+    if constexpr (KIND == kInt4Page) {
+      c[t / 2] += corr[t / 2];
+      if constexpr (NG == 2) c[t / 2 + 2] += corr[t / 2 + 2];
+    }
+    c = mfma(a_hi, bv, c);
+    c = mfma(a_lo, bv, c);
+    u.o[t] = c;
+  }
+}
+
+// Runs n tiles (ptr(i), mask(i)) two at a time, loading the next pair while
+// computing the current one.  Tile n (odd n) is a masked copy of tile n-1.
+template <int KIND, int D, class PtrFn, class MaskFn>
+__device__ inline void run_tiles(Unit<D>& u, int n, PtrFn ptr, MaskFn mask, int lane) {
+  if (n <= 0) return;
+  const int ln = lane & 15, kg = lane >> 4;
+  const int nsteps = (n + 1) >> 1;
+  Tile<KIND, D> a0, a1, b0, b1;
+  a0.load(ptr(0), ln, kg);
+  a1.load(ptr(n > 1 ? 1 : 0), ln, kg);
+  for (int s = 0; s < nsteps; s += 2) {
+    if (s + 1 < nsteps) {
+      const int i = 2 * (s + 1);
+      b0.load(ptr(i), ln, kg);
+      b1.load(ptr(i + 1 < n ? i + 1 : i), ln, kg);
+    }
+    step<KIND, D>(u, a0, a1, mask(2 * s), 2 * s + 1 < n ? mask(2 * s + 1) : 0u, lane);
+    if (s + 1 >= nsteps) break;
+    if (s + 2 < nsteps) {
+      const int i = 2 * (s + 2);
+      a0.load(ptr(i), ln, kg);
+      a1.load(ptr(i + 1 < n ? i + 1 : i), ln, kg);
+    }
+    step<KIND, D>(u, b0, b1, mask(2 * s + 2), 2 * s + 3 < n ? mask(2 * s + 3) : 0u, lane);
+  }
+}
+
+__device__ inline uint32_t range_mask(int lo, int hi) {  // bits [lo, hi) of 0..15
+  lo = lo < 0 ? 0 : lo;
+  hi = hi > 16 ? 16 : hi;
+  if (hi <= lo) return 0u;
+  return ((1u << hi) - 1u) & ~((1u << lo) - 1u);
+}
 
 // ---------------------------------------------------------------- worklist --
-__device__ inline int items_of(int L, int S, int R, int chunk_pages, int* mid_first_page, int* mid_last_page) {
-  Regions g = regions(L, S, R);
+__device__ inline int items_of(int L, int S, int R, int chunk_pages) {
+  const Regions g = regions(L, S, R);
   int np = 0;
-  if (g.me > g.mb) {
-    *mid_first_page = g.mb / kPage;
-    *mid_last_page = (g.me - 1) / kPage;
-    np = *mid_last_page - *mid_first_page + 1;
-  } else {
-    *mid_first_page = 0;
-    *mid_last_page = -1;
-  }
-  int n = (np + chunk_pages - 1) / chunk_pages;
+  if (g.me > g.mb) np = (g.me - 1) / kPage - g.mb / kPage + 1;
+  const int n = (np + chunk_pages - 1) / chunk_pages;
   return n < 1 ? 1 : n;
 }
 
@@ -45,16 +410,16 @@ __global__ __launch_bounds__(1024) void worklist_kernel(DecodeParams p) {
   __syncthreads();
   for (int base = 0; base < p.batch; base += 1024) {
     const int b = base + tid;
-    int n = 0, f, l;
+    int n = 0;
     if (b < p.batch) {
       int L = p.seq_lens[b];
       L = L < 0 ? 0 : (L > p.max_pages * kPage ? p.max_pages * kPage : L);
-      n = items_of(L, p.n_sink, p.n_recent, p.chunk_pages, &f, &l);
+      n = items_of(L, p.n_sink, p.n_recent, p.chunk_pages);
     }
     scan[tid] = n;
     __syncthreads();
     for (int o = 1; o < 1024; o <<= 1) {  // inclusive Hillis-Steele scan
-      int v = tid >= o ? scan[tid - o] : 0;
+      const int v = tid >= o ? scan[tid - o] : 0;
       __syncthreads();
       scan[tid] += v;
       __syncthreads();
@@ -75,169 +440,145 @@ __global__ __launch_bounds__(1024) void worklist_kernel(DecodeParams p) {
   }
 }
 
-// ------------------------------------------------------- row dequantization --
-template <int E>
-__device__ inline void load_int8_row(const uint8_t* __restrict__ tile, int r, int lane, float (&k)[E],
-                                     float (&v)[E]) {
-  constexpr int D = E * kWave;
-  const float sk = f16_to_f32(*reinterpret_cast<const uint16_t*>(tile + k8_scale(D, r)));
-  const float sv = f16_to_f32(*reinterpret_cast<const uint16_t*>(tile + v8_scale(D, r)));
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const int c = lane * E + e;
-    k[e] = float(int8_t(tile[k8_byte(D, r, c)])) * sk;
-    v[e] = float(int8_t(tile[v8_byte(D, r, c)])) * sv;
-  }
-}
-
-__device__ inline int nibble(uint8_t b, int high) {
-  int n = high ? (b >> 4) : (b & 15);
-  return n >= 8 ? n - 16 : n;
-}
-
-template <int E>
-__device__ inline void load_int4_row(const uint8_t* __restrict__ blk, int r, int lane, float (&k)[E],
-                                     float (&v)[E]) {
-  constexpr int D = E * kWave;
-  const int grp = (lane * E) / kGroup;
-  const float sk = f16_to_f32(*reinterpret_cast<const uint16_t*>(blk + k4_scale(D, r, grp)));
-  const float sv = f16_to_f32(*reinterpret_cast<const uint16_t*>(blk + v4_scale(D, r, grp)));
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const int c = lane * E + e;
-    k[e] = float(nibble(blk[k4_byte(D, r, c)], c & 1)) * sk;
-    v[e] = float(nibble(blk[v4_byte(D, r, c)], (c / 16) & 1)) * sv;
-  }
-}
-
-template <int E>
-__device__ inline void load_bf16_row(const uint8_t* __restrict__ tile, int r, int lane, float (&k)[E],
-                                     float (&v)[E]) {
-  constexpr int D = E * kWave;
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const int c = lane * E + e;
-    k[e] = bf16_to_f32(*reinterpret_cast<const uint16_t*>(tile + kb_byte(D, r, c)));
-    v[e] = bf16_to_f32(*reinterpret_cast<const uint16_t*>(tile + vb_byte(D, r, c)));
-  }
-}
-
-// ------------------------------------------------------------- attention ---
-template <int E, int G>
-struct Online {
-  float q[G][E];
-  float m[G], l[G], o[G][E];
-
-  __device__ inline void init() {
-#pragma unroll
-    for (int j = 0; j < G; ++j) {
-      m[j] = -INFINITY;
-      l[j] = 0.f;
-#pragma unroll
-      for (int e = 0; e < E; ++e) o[j][e] = 0.f;
-    }
-  }
-  // One position: scores for the G heads, online softmax update.
-  __device__ inline void step(const float (&k)[E], const float (&v)[E], float sm) {
-#pragma unroll
-    for (int j = 0; j < G; ++j) {
-      float d = 0.f;
-#pragma unroll
-      for (int e = 0; e < E; ++e) d = fmaf(q[j][e], k[e], d);
-      d = wave_sum<kWave>(d) * sm;
-      const float mn = fmaxf(m[j], d);
-      const float a = __expf(m[j] - mn);
-      const float pj = __expf(d - mn);
-      l[j] = l[j] * a + pj;
-#pragma unroll
-      for (int e = 0; e < E; ++e) o[j][e] = fmaf(pj, v[e], o[j][e] * a);
-      m[j] = mn;
-    }
-  }
-};
-
-template <int FMT, int E, int G>
+// ------------------------------------------------------------- attention --
+template <int FMT, int D>
 __global__ __launch_bounds__(256) void attention_kernel(DecodeParams p) {
-  constexpr int D = E * kWave;
+  constexpr int NG = D / 32, HB = 16 / NG, NT = D / 16;
+  constexpr int MAIN = FMT == kFmtKV4 ? kInt4Page : (FMT == kFmtKV8 ? kInt8Tile : kBf16Page);
   const int lane = threadIdx.x & (kWave - 1);
-  const int H = p.num_kv_heads, Hq = p.num_q_heads;
+  const int ln = lane & 15, kg = lane >> 4;
+  const int H = p.num_kv_heads, Hq = p.num_q_heads, G = Hq / H;
+  const int NHB = (G + HB - 1) / HB;
   const int S = FMT == kFmtKV4 ? p.n_sink : 0;
   const int R = FMT == kFmtKV4 ? p.n_recent : 0;
-  const int64_t units = int64_t(p.ws.header[1]) * H;
+  const int64_t units = int64_t(p.ws.header[1]) * H * NHB;
+
   for (;;) {
-    int64_t u = 0;
-    if (lane == 0) u = atomicAdd(&p.ws.header[0], 1u);
-    u = __shfl(int(u), 0, kWave);
-    if (u >= units) break;
-    const int2 it = p.ws.items[u / H];
-    const int h = int(u % H);
+    int ui = 0;
+    if (lane == 0) ui = int(atomicAdd(&p.ws.header[0], 1u));
+    const int64_t uu = __shfl(ui, 0, kWave);
+    if (uu >= units) break;
+    const int64_t item = uu / (H * NHB);
+    const int rem = int(uu % (H * NHB));
+    const int h = rem / NHB, hb = rem % NHB;
+    const int2 it = p.ws.items[item];
     const int b = it.x, chunk = it.y;
     int L = p.seq_lens[b];
     L = L < 0 ? 0 : (L > p.max_pages * kPage ? p.max_pages * kPage : L);
     const Regions g = regions(L, S, R);
 
-    Online<E, G> st;
-    st.init();
+    // ---- unit set-up: q operand of this lane's row (head hl, group grp)
+    Unit<D> u;
+    {
+      const int hl = ln / NG, grp = ln % NG;
+      const int j = hb * HB + hl;
+      const bool valid = j < G;
+      const bool take = valid && ((NG == 4 ? kg : (kg >> 1)) == grp);
+      const uint16_t* qrow = p.q + (int64_t(b) * Hq + h * G + (valid ? j : 0)) * D;
 #pragma unroll
-    for (int j = 0; j < G; ++j)
-#pragma unroll
-      for (int e = 0; e < E; ++e)
-        st.q[j][e] = bf16_to_f32(p.q[(int64_t(b) * Hq + h * G + j) * D + lane * E + e]);
-
-    float k[E], v[E];
-    if (FMT == kFmtKV4 && chunk == 0 && (g.se > 0 || g.rb < L)) {
-      const int slot = p.slot_ids ? p.slot_ids[b] : b;
-      if (slot >= 0 && slot < p.num_slots) {
-        const uint8_t* sblk = p.side + (int64_t(slot) * H + h) * p.side_bytes;
-        for (int pos = 0; pos < L; ++pos) {
-          if (pos == g.se) pos = g.rb;  // skip the middle
-          if (pos >= L) break;
-          const int row = side_row(pos, S, R);
-          load_int8_row<E>(sblk + int64_t(row / kPage) * int8_tile_bytes(D), row % kPage, lane, k, v);
-          st.step(k, v, p.softmax_scale);
+      for (int t = 0; t < NG; ++t) {
+        uint32_t w0 = 0, w1 = 0, w2 = 0, w3 = 0;
+        if (take) {
+          const uint4 a = *reinterpret_cast<const uint4*>(qrow + kg * (D / 4) + 8 * t);
+          w0 = a.x; w1 = a.y; w2 = a.z; w3 = a.w;
+        }
+        if constexpr (MAIN == kBf16Page) {
+          u.bq[t] = bf8(w0, w1, w2, w3);  // channels in natural order
+        } else {
+          // element pairs (c, c+4): the order the code conversions produce
+          u.bq[t] = bf8(__builtin_amdgcn_perm(w2, w0, 0x05040100u), __builtin_amdgcn_perm(w2, w0, 0x07060302u),
+                        __builtin_amdgcn_perm(w3, w1, 0x05040100u), __builtin_amdgcn_perm(w3, w1, 0x07060302u));
         }
       }
+      double qs = 0.0;
+      if (MAIN == kInt4Page && valid) {
+#pragma unroll
+        for (int c = 0; c < 32; ++c) qs += double(bf16_to_f32(qrow[grp * 32 + c]));
+      }
+      u.qsum = float(qs);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) u.o[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      u.m = -INFINITY;
+      u.l = 0.f;
+      u.qk_scale = p.softmax_scale * kLog2e;
     }
+
+    // ---- protected rows: INT8 side-cache tiles (sinks, then the ring)
+    if (FMT == kFmtKV4 && chunk == 0 && L > 0 && S + R > 0) {
+      const int slot = p.slot_ids ? p.slot_ids[b] : b;
+      if (slot >= 0 && slot < p.num_slots) {
+        const int se = L < S ? L : S;
+        const int nring = L > S ? (L - S < R ? L - S : R) : 0;
+        const int rows = nring > 0 ? S + nring : se;
+        const int ntiles = (rows + kPage - 1) / kPage;
+        const uint8_t* sblk = p.side + (int64_t(slot) * H + h) * p.side_bytes;
+        auto ptr = [&](int i) { return sblk + int64_t(i) * int8_tile_bytes(D); };
+        auto mask = [&](int i) {
+          const int r0 = i * kPage;
+          return range_mask(0 - r0, se - r0) | range_mask(S - r0, S + nring - r0);
+        };
+        run_tiles<kInt8Tile, D>(u, ntiles, ptr, mask, lane);
+      }
+    }
+
+    // ---- middle pages of this chunk
     if (g.me > g.mb) {
       const int first = g.mb / kPage + chunk * p.chunk_pages;
       int last = first + p.chunk_pages - 1;
       if (last > (g.me - 1) / kPage) last = (g.me - 1) / kPage;
-      for (int pg = first; pg <= last; ++pg) {
-        const int64_t pid = p.page_table[int64_t(b) * p.max_pages + pg];
-        if (pid < 0 || pid >= p.num_pages) continue;
-        const uint8_t* blk = p.pages + (pid * H + h) * p.block_bytes;
-        for (int r = 0; r < kPage; ++r) {
-          const int pos = pg * kPage + r;
-          if (pos < g.mb || pos >= g.me) continue;
-          if constexpr (FMT == kFmtKV4) load_int4_row<E>(blk, r, lane, k, v);
-          else if constexpr (FMT == kFmtKV8) load_int8_row<E>(blk, r, lane, k, v);
-          else load_bf16_row<E>(blk, r, lane, k, v);
-          st.step(k, v, p.softmax_scale);
+      const int npg = last - first + 1;
+      int pid_l = 0;
+      if (lane < npg) {
+        const int64_t v = p.page_table[int64_t(b) * p.max_pages + first + lane];
+        pid_l = (v < 0 || v >= p.num_pages) ? -1 : int(v);
+      }
+      auto ptr = [&](int i) {
+        const int pid = __builtin_amdgcn_readlane(pid_l, i);
+        return p.pages + (int64_t(pid < 0 ? 0 : pid) * H + h) * p.block_bytes;
+      };
+      auto mask = [&](int i) {
+        const int pid = __builtin_amdgcn_readlane(pid_l, i);
+        const int p0 = (first + i) * kPage;
+        return pid < 0 ? 0u : range_mask(g.mb - p0, g.me - p0);
+      };
+      run_tiles<MAIN, D>(u, npg, ptr, mask, lane);
+    }
+
+    // ---- finish: per-head denominators, then output or partial
+    float lt = u.l;
+    lt += __shfl_xor(lt, 16, kWave);
+    lt += __shfl_xor(lt, 32, kWave);
+    const int nitems = p.ws.item_count[b];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+#pragma unroll
+      for (int k = 0; k < (NG == 4 ? 1 : 2); ++k) {
+        const int e = t / 2 + 2 * k;
+        const float lh = head_value_for_acc<D>(lt, lane, e);
+        const int hl = NG == 4 ? (lane >> 4) : ((lane >> 4) * 2 + k);
+        const int j = hb * HB + hl;
+        if (j < G) {
+          const int hq = h * G + j;
+          const int c = 16 * t + ln;
+          if (nitems == 1) {
+            const float v = lh > 0.f ? 16.0f * u.o[t][e] / lh : 0.f;
+            p.out[(int64_t(b) * Hq + hq) * D + c] = f32_to_bf16_bits(v);
+          } else {
+            p.ws.partials[((int64_t(p.ws.item_base[b]) + chunk) * Hq + hq) * (D + 2) + c] = 16.0f * u.o[t][e];
+          }
         }
       }
     }
-
-    const int nitems = p.ws.item_count[b];
-    if (nitems == 1) {
-#pragma unroll
-      for (int j = 0; j < G; ++j) {
+    if (kg == 0 && (ln % NG) == 0) {
+      const int j = hb * HB + ln / NG;
+      if (j < G) {
         const int hq = h * G + j;
-        const float inv = st.l[j] > 0.f ? 1.0f / st.l[j] : 0.f;
-#pragma unroll
-        for (int e = 0; e < E; ++e)
-          p.out[(int64_t(b) * Hq + hq) * D + lane * E + e] = f32_to_bf16_bits(st.o[j][e] * inv);
-        if (p.lse && lane == 0) p.lse[int64_t(b) * Hq + hq] = st.l[j] > 0.f ? st.m[j] + logf(st.l[j]) : -INFINITY;
-      }
-    } else {
-      const int64_t slot = int64_t(p.ws.item_base[b] + chunk) * Hq;
-#pragma unroll
-      for (int j = 0; j < G; ++j) {
-        float* part = p.ws.partials + (slot + h * G + j) * (D + 2);
-#pragma unroll
-        for (int e = 0; e < E; ++e) part[lane * E + e] = st.o[j][e];
-        if (lane == 0) {
-          part[D] = st.m[j];
-          part[D + 1] = st.l[j];
+        if (nitems == 1) {
+          if (p.lse) p.lse[int64_t(b) * Hq + hq] = lt > 0.f ? (u.m + log2f(lt)) * kLn2 : -INFINITY;
+        } else {
+          float* part = p.ws.partials + ((int64_t(p.ws.item_base[b]) + chunk) * Hq + hq) * (D + 2);
+          part[D] = u.m;
+          part[D + 1] = lt;
         }
       }
     }
@@ -245,9 +586,9 @@ __global__ __launch_bounds__(256) void attention_kernel(DecodeParams p) {
 }
 
 // ----------------------------------------------------------------- merge ---
-template <int E>
+template <int D>
 __global__ __launch_bounds__(256) void merge_kernel(DecodeParams p) {
-  constexpr int D = E * kWave;
+  constexpr int E = D / kWave;
   const int lane = threadIdx.x & (kWave - 1);
   const int Hq = p.num_q_heads;
   const int64_t w = int64_t(blockIdx.x) * (blockDim.x / kWave) + threadIdx.x / kWave;
@@ -257,15 +598,18 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeParams p) {
   if (n <= 1) return;
   const int64_t base = int64_t(p.ws.item_base[b]) * Hq + hq;
   float M = -INFINITY;
-  for (int i = 0; i < n; ++i) M = fmaxf(M, p.ws.partials[(base + int64_t(i) * Hq) * (D + 2) + D]);
+  for (int i = 0; i < n; ++i) {
+    const float* part = p.ws.partials + (base + int64_t(i) * Hq) * (D + 2);
+    if (part[D + 1] > 0.f) M = fmaxf(M, part[D]);
+  }
   float l = 0.f, o[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) o[e] = 0.f;
   for (int i = 0; i < n; ++i) {
     const float* part = p.ws.partials + (base + int64_t(i) * Hq) * (D + 2);
     const float li = part[D + 1];
-    if (li <= 0.f) continue;  // empty item
-    const float a = __expf(part[D] - M);
+    if (!(li > 0.f)) continue;  // an item without context rows
+    const float a = exp2f(part[D] - M);
     l += a * li;
 #pragma unroll
     for (int e = 0; e < E; ++e) o[e] = fmaf(a, part[lane * E + e], o[e]);
@@ -273,51 +617,42 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeParams p) {
   const float inv = l > 0.f ? 1.0f / l : 0.f;
 #pragma unroll
   for (int e = 0; e < E; ++e) p.out[(int64_t(b) * Hq + hq) * D + lane * E + e] = f32_to_bf16_bits(o[e] * inv);
-  if (p.lse && lane == 0) p.lse[int64_t(b) * Hq + hq] = l > 0.f ? M + logf(l) : -INFINITY;
+  if (p.lse && lane == 0) p.lse[int64_t(b) * Hq + hq] = l > 0.f ? (M + log2f(l)) * kLn2 : -INFINITY;
 }
 
 // --------------------------------------------------------------- launch ---
-int persistent_blocks(const void* kernel) {
+template <class K>
+int persistent_blocks(K kernel) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
   int cus = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
   int per_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, 0) != hipSuccess || per_cu < 1)
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(kernel), 256, 0) !=
+          hipSuccess ||
+      per_cu < 1)
     per_cu = 1;
   return cus * per_cu;
 }
 
-template <int FMT, int E, int G>
-hipError_t launch_g(const DecodeParams& p, hipStream_t stream) {
+template <int FMT, int D>
+hipError_t launch_fd(const DecodeParams& p, hipStream_t stream) {
   hipLaunchKernelGGL(worklist_kernel, dim3(1), dim3(1024), 0, stream, p);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const void* k = reinterpret_cast<const void*>(&attention_kernel<FMT, E, G>);
-  const int blocks = persistent_blocks(k);
+  const int blocks = persistent_blocks(attention_kernel<FMT, D>);
   if (blocks <= 0) return hipErrorInvalidDevice;
-  hipLaunchKernelGGL((attention_kernel<FMT, E, G>), dim3(blocks), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((attention_kernel<FMT, D>), dim3(blocks), dim3(256), 0, stream, p);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   const int64_t waves = int64_t(p.batch) * p.num_q_heads;
-  hipLaunchKernelGGL((merge_kernel<E>), dim3(unsigned((waves + 3) / 4)), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((merge_kernel<D>), dim3(unsigned((waves + 3) / 4)), dim3(256), 0, stream, p);
   return hipGetLastError();
-}
-
-template <int FMT, int E>
-hipError_t launch_e(const DecodeParams& p, hipStream_t stream) {
-  switch (p.num_q_heads / p.num_kv_heads) {
-    case 1: return launch_g<FMT, E, 1>(p, stream);
-    case 2: return launch_g<FMT, E, 2>(p, stream);
-    case 4: return launch_g<FMT, E, 4>(p, stream);
-    case 8: return launch_g<FMT, E, 8>(p, stream);
-    default: return hipErrorInvalidValue;
-  }
 }
 
 template <int FMT>
 hipError_t launch_fmt(const DecodeParams& p, int head_dim, hipStream_t stream) {
-  return head_dim == 128 ? launch_e<FMT, 2>(p, stream) : launch_e<FMT, 1>(p, stream);
+  return head_dim == 128 ? launch_fd<FMT, 128>(p, stream) : launch_fd<FMT, 64>(p, stream);
 }
 
 }  // namespace
@@ -326,9 +661,13 @@ int32_t decode_chunk_pages() { return kChunkPages; }
 
 static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-size_t decode_workspace_bytes(int32_t batch, int32_t max_pages, int32_t num_q_heads, int32_t head_dim) {
+static int64_t max_items_of(int32_t batch, int32_t max_pages) {
   const int64_t per_seq = (int64_t(max_pages) + kChunkPages - 1) / kChunkPages;
-  const int64_t max_items = int64_t(batch) * (per_seq < 1 ? 1 : per_seq);
+  return int64_t(batch) * (per_seq < 1 ? 1 : per_seq);
+}
+
+size_t decode_workspace_bytes(int32_t batch, int32_t max_pages, int32_t num_q_heads, int32_t head_dim) {
+  const int64_t max_items = max_items_of(batch, max_pages);
   size_t s = 256;                                   // header
   s += align256(sizeof(int32_t) * size_t(batch));  // item_base
   s += align256(sizeof(int32_t) * size_t(batch));  // item_count
@@ -339,22 +678,21 @@ size_t decode_workspace_bytes(int32_t batch, int32_t max_pages, int32_t num_q_he
 
 DecodeWorkspace carve_workspace(void* base, int32_t batch, int32_t max_pages, int32_t num_q_heads,
                                 int32_t head_dim) {
-  const int64_t per_seq = (int64_t(max_pages) + kChunkPages - 1) / kChunkPages;
-  const int64_t max_items = int64_t(batch) * (per_seq < 1 ? 1 : per_seq);
-  uint8_t* p = static_cast<uint8_t*>(base);
-  DecodeWorkspace w;
-  w.header = reinterpret_cast<uint32_t*>(p);
-  p += 256;
-  w.item_base = reinterpret_cast<int32_t*>(p);
-  p += align256(sizeof(int32_t) * size_t(batch));
-  w.item_count = reinterpret_cast<int32_t*>(p);
-  p += align256(sizeof(int32_t) * size_t(batch));
-  w.items = reinterpret_cast<int2*>(p);
-  p += align256(sizeof(int2) * size_t(max_items));
-  w.partials = reinterpret_cast<float*>(p);
-  w.max_items = max_items;
   (void)num_q_heads;
   (void)head_dim;
+  const int64_t max_items = max_items_of(batch, max_pages);
+  uint8_t* q = static_cast<uint8_t*>(base);
+  DecodeWorkspace w;
+  w.header = reinterpret_cast<uint32_t*>(q);
+  q += 256;
+  w.item_base = reinterpret_cast<int32_t*>(q);
+  q += align256(sizeof(int32_t) * size_t(batch));
+  w.item_count = reinterpret_cast<int32_t*>(q);
+  q += align256(sizeof(int32_t) * size_t(batch));
+  w.items = reinterpret_cast<int2*>(q);
+  q += align256(sizeof(int2) * size_t(max_items));
+  w.partials = reinterpret_cast<float*>(q);
+  w.max_items = max_items;
   return w;
 }
 
