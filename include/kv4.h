@@ -25,6 +25,10 @@
  *     streams are independent as long as they do not write the same pages,
  *     side blocks, outputs or workspace.
  *   - bf16 / fp16 values are passed as their raw 16-bit patterns (uint16_t).
+ *   - Page pools and side caches must be zero-filled when first allocated.
+ *     Decode reads whole pages and tiles; rows outside a sequence's context
+ *     get weight 0, which is exact only if their bytes are finite numbers --
+ *     true for zero fill and for anything append ever wrote.
  *
  * Cache layout (readings: the pages say only "paged INT4" plus an INT8 side
  * cache of at most 144 positions, [NEWS] Interpretation para 3, [ART]):
@@ -106,8 +110,8 @@ const char* kv4_status_string(kv4_status status); /* static string, never NULL *
 /* INT4 page block per (page, kv head), 18 * head_dim bytes (D = head_dim,
  * r = position mod 16, c = channel, q4 = r/4, rr = r%4, t = c/16, n = c%16):
  *   K codes  [0, 8D)    byte r*(D/2) + c/2, low nibble = even channel
- *   V codes  [8D, 16D)  byte (q4*16 + n)*(D/8) + rr*(D/32) + t/2,
- *                       low nibble = even t
+ *   V codes  [8D, 16D)  byte (q4*16 + n)*(D/8) + 4*((rr/2)*(D/64) + t/4)
+ *                       + 2*(rr%2) + (t%4)/2, low nibble = even t
  *   K scales [16D, 17D) fp16 at byte (grp*16 + r)*2, grp = c/32
  *   V scales [17D, 18D) fp16 likewise
  * Nibbles are two's complement.  Returns 0 for an unsupported layout. */
@@ -170,6 +174,7 @@ kv4_status kv4_decode_workspace_size(const kv4_layout* layout, int32_t batch,
  *   q      bf16 [batch][num_q_heads][head_dim]
  *   out    bf16 [batch][num_q_heads][head_dim] (rounded to nearest even)
  *   lse    fp32 [batch][num_q_heads] natural-log sum of exp, or NULL
+ * softmax_scale must be positive and finite (KV4_ERR_INVALID_ARG otherwise).
  * L = 0 gives out = 0 and lse = -inf.  Arithmetic: exact dequantized
  * products, fp32 accumulation.  The workspace is scratch for this call. */
 kv4_status kv4_decode_attention(const kv4_layout* layout, const kv4_cache* cache,

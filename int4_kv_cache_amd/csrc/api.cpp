@@ -98,6 +98,7 @@ kv4_status decode_impl(int fmt, const kv4_layout* L, const kv4_cache* c, const k
   if (s != KV4_OK) return s;
   if (b->batch == 0) return KV4_OK;
   if (!q || !out || !ws) return KV4_ERR_INVALID_ARG;
+  if (!(sm > 0.0f) || sm > 3.0e38f) return KV4_ERR_INVALID_ARG;  // positive and finite
   const size_t need = kv4::decode_workspace_bytes(b->batch, b->max_pages, L->num_q_heads, L->head_dim);
   if (ws_bytes < need) return KV4_ERR_WORKSPACE;
   kv4::DecodeParams p{};
@@ -120,7 +121,6 @@ kv4_status decode_impl(int fmt, const kv4_layout* L, const kv4_cache* c, const k
   p.n_recent = fmt == kFmtKV4 ? L->n_recent : 0;
   p.block_bytes = int64_t(block_bytes(L, fmt));
   p.side_bytes = int64_t(side_bytes(L));
-  p.chunk_pages = kv4::decode_chunk_pages();
   p.ws = kv4::carve_workspace(ws, b->batch, b->max_pages, L->num_q_heads, L->head_dim);
   if (!protected_set(L, fmt)) {
     p.side = nullptr;

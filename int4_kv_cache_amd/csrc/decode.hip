@@ -37,7 +37,20 @@ typedef __bf16 bf16x8_t __attribute__((__vector_size__(16)));
 typedef float f32x4_t __attribute__((__vector_size__(16)));
 typedef uint32_t u32x4_t __attribute__((__vector_size__(16)));
 
-constexpr int kChunkPages = 32;  // middle pages per work item (<= 64)
+#ifndef KV4_CHUNK_PAGES
+#define KV4_CHUNK_PAGES 32
+#endif
+#ifndef KV4_WAVES_PER_EU
+#define KV4_WAVES_PER_EU 2
+#endif
+#ifndef KV4_STAGES
+#define KV4_STAGES 3  // pipeline depth of the INT4 page loop
+#endif
+#ifndef KV4_STAGES8
+#define KV4_STAGES8 2  // pipeline depth of the INT8 tile loops
+#endif
+constexpr int kChunkPages = KV4_CHUNK_PAGES;  // middle pages per work item (<= 64)
+static_assert(kChunkPages >= 1 && kChunkPages <= 64, "one lane holds one page id");
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescale = 8.0f;  // re-reference the running max when it grows by 2^8
@@ -75,12 +88,21 @@ __device__ inline uint32_t nib_pair(uint32_t d) {
   const uint32_t x = K == 0 ? (d << 3) : (d >> (4 * K - 3));
   return (x & 0x00780078u) ^ 0x3FC03FC0u;
 }
-// INT4 V: x holds one byte at bits 0-7 and one at 16-23; take the low (HIGH
-// = false) or high nibble of each as a bf16 pair 1 + (code+8)/16.
-template <bool HIGH>
-__device__ inline uint32_t vnib_pair(uint32_t x) {
-  const uint32_t y = HIGH ? (x >> 1) : (x << 3);
-  return (y & 0x00780078u) ^ 0x3FC03FC0u;
+__device__ inline uint32_t nib_pair_at(uint32_t d, int k) {  // k in 0..3 (unrolled)
+  switch (k) {
+    case 0: return nib_pair<0>(d);
+    case 1: return nib_pair<1>(d);
+    case 2: return nib_pair<2>(d);
+    default: return nib_pair<3>(d);
+  }
+}
+
+// Cross-lane moves inside groups of 4 lanes (DPP quad permutations).
+__device__ inline float quad_xor1(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));
+}
+__device__ inline float quad_xor2(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true));
 }
 
 // ------------------------------------------------------------ tile loads --
@@ -170,7 +192,8 @@ struct Unit {
   float qk_scale;                    // softmax_scale * log2(e)
 };
 
-// QK for one tile -> x[e] = scaled per-group partial score of position 4kg+e.
+// QK for one tile -> x[e] = per-group partial score of position 4kg+e, before
+// the softmax scale (and, for INT4, before the factor 16 of the encoding).
 template <int KIND, int D>
 __device__ inline void qk_tile(const Unit<D>& u, const Tile<KIND, D>& T, float (&x)[4]) {
   constexpr int NG = D / 32;
@@ -200,48 +223,34 @@ __device__ inline void qk_tile(const Unit<D>& u, const Tile<KIND, D>& T, float (
   }
   if constexpr (KIND == kBf16Page) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) x[e] = acc[e] * u.qk_scale;
+    for (int e = 0; e < 4; ++e) x[e] = acc[e];
   } else {
-    const float s = KIND == kInt4Page ? 16.0f * u.qk_scale : u.qk_scale;
-    x[0] = acc[0] * h2f_lo(T.ks[0]) * s;
-    x[1] = acc[1] * h2f_hi(T.ks[0]) * s;
-    x[2] = acc[2] * h2f_lo(T.ks[1]) * s;
-    x[3] = acc[3] * h2f_hi(T.ks[1]) * s;
+    x[0] = acc[0] * h2f_lo(T.ks[0]);
+    x[1] = acc[1] * h2f_hi(T.ks[0]);
+    x[2] = acc[2] * h2f_lo(T.ks[1]);
+    x[3] = acc[3] * h2f_hi(T.ks[1]);
   }
 }
 
-
-// Zero mask of the two bf16 halves of a position pair: a half is cleared when
-// its position is not part of the context (bf16 pages only: unused rows may
-// hold any bit pattern, and 0 * NaN would poison the accumulator).
-__device__ inline uint32_t pair_zero_mask(uint32_t valid4, int r) {
-  return (((valid4 >> r) & 1u) ? 0u : 0x0000FFFFu) | (((valid4 >> (r + 1)) & 1u) ? 0u : 0xFFFF0000u);
-}
-
 // V operand of PV N-tile t from two tiles: positions 4kg..4kg+3 of T0 then of
-// T1, channel 16t + ln.  valid0/valid1: the lane's 4 position bits per tile.
+// T1, channel 16t + ln.  Rows outside the context get p = 0; their bytes are
+// finite (written by append, or the zero fill the pools start from), so they
+// contribute exactly 0.
 template <int KIND, int D>
-__device__ inline bf16x8_t v_operand(const Tile<KIND, D>& T0, const Tile<KIND, D>& T1, int t,
-                                     uint32_t valid0, uint32_t valid1) {
+__device__ inline bf16x8_t v_operand(const Tile<KIND, D>& T0, const Tile<KIND, D>& T1, int t) {
   if constexpr (KIND == kInt4Page) {
-    // position rr's D/32 bytes start at byte rr*(D/32); channel 16t+n is
-    // nibble t of them: byte t/2, low nibble for even t.
-    constexpr int PB = D / 32;
-    auto pair = [&](const Tile<KIND, D>& T, int r0) -> uint32_t {
-      const int o0 = r0 * PB + t / 2, o1 = (r0 + 1) * PB + t / 2;
-      const uint32_t a = T.v[o0 >> 2], b = T.v[o1 >> 2];
-      const uint32_t sel = uint32_t(o0 & 3) | (0x0Cu << 8) | (uint32_t(4 + (o1 & 3)) << 16) | (0x0Cu << 24);
-      const uint32_t x = __builtin_amdgcn_perm(b, a, sel);
-      return (t & 1) ? vnib_pair<true>(x) : vnib_pair<false>(x);
-    };
-    return bf8(pair(T0, 0), pair(T0, 2), pair(T1, 0), pair(T1, 2));
+    // word (pair*(D/64) + t/4) holds channel 16t+n of positions (2 pair,
+    // 2 pair + 1) as nibble t%4 of its low and high half.
+    constexpr int QW = D / 64;
+    const int j = t & 3, w = t >> 2;
+    return bf8(nib_pair_at(T0.v[w], j), nib_pair_at(T0.v[QW + w], j), nib_pair_at(T1.v[w], j),
+               nib_pair_at(T1.v[QW + w], j));
   } else if constexpr (KIND == kInt8Tile) {
     const uint32_t a = T0.v[t], b = T1.v[t];
     return bf8(pack_exact(sbyte(a, 0), sbyte(a, 1)), pack_exact(sbyte(a, 2), sbyte(a, 3)),
                pack_exact(sbyte(b, 0), sbyte(b, 1)), pack_exact(sbyte(b, 2), sbyte(b, 3)));
   } else {
-    return bf8(T0.v[2 * t] & ~pair_zero_mask(valid0, 0), T0.v[2 * t + 1] & ~pair_zero_mask(valid0, 2),
-               T1.v[2 * t] & ~pair_zero_mask(valid1, 0), T1.v[2 * t + 1] & ~pair_zero_mask(valid1, 2));
+    return bf8(T0.v[2 * t], T0.v[2 * t + 1], T1.v[2 * t], T1.v[2 * t + 1]);
   }
 }
 
@@ -258,7 +267,7 @@ __device__ inline float head_value_for_acc(float v, int lane, int e) {
 }
 
 // One step: two 16-row tiles (32 positions).  mask0/mask1: 16-bit row masks.
-template <int KIND, int D>
+template <int KIND, int D, bool MASKED>
 __device__ inline void step(Unit<D>& u, const Tile<KIND, D>& T0, const Tile<KIND, D>& T1, uint32_t mask0,
                             uint32_t mask1, int lane) {
   constexpr int NG = D / 32;
@@ -269,31 +278,36 @@ __device__ inline void step(Unit<D>& u, const Tile<KIND, D>& T0, const Tile<KIND
   float x0[4], x1[4];
   qk_tile<KIND, D>(u, T0, x0);
   qk_tile<KIND, D>(u, T1, x1);
+  // sum the per-group partial scores of a head (lanes 4h..4h+3 or 2h..2h+1)
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    x0[e] += __shfl_xor(x0[e], 1, kWave);
-    x1[e] += __shfl_xor(x1[e], 1, kWave);
+    x0[e] += quad_xor1(x0[e]);
+    x1[e] += quad_xor1(x1[e]);
     if constexpr (NG == 4) {
-      x0[e] += __shfl_xor(x0[e], 2, kWave);
-      x1[e] += __shfl_xor(x1[e], 2, kWave);
+      x0[e] += quad_xor2(x0[e]);
+      x1[e] += quad_xor2(x1[e]);
     }
   }
   float mx = -INFINITY;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    x0[e] = ((va0 >> e) & 1u) ? x0[e] : -INFINITY;
-    x1[e] = ((va1 >> e) & 1u) ? x1[e] : -INFINITY;
+    if constexpr (MASKED) {
+      x0[e] = ((va0 >> e) & 1u) ? x0[e] : -INFINITY;
+      x1[e] = ((va1 >> e) & 1u) ? x1[e] : -INFINITY;
+    }
     mx = fmaxf(mx, fmaxf(x0[e], x1[e]));
   }
-  mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-  mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+  // score (log2 units) = sc * x; INT4 partials carry the encoding's 1/16
+  const float sc = KIND == kInt4Page ? 16.0f * u.qk_scale : u.qk_scale;
 
-  // Re-reference the running max only when it grew by 2^kRescale: p stays
-  // below 2^8, and the accumulators are rescaled rarely.
-  const bool need = mx > u.m + kRescale;
-  if (__any(need)) {
-    const float mn = fmaxf(u.m, mx);
-    const float alpha = (mn == u.m) ? 1.0f : exp2f(u.m - mn);
+  // The running max of a head is only re-referenced when a score exceeds it
+  // by 2^kRescale (then to the head's exact maximum so far), so p <= 2^8 and
+  // the accumulators are rescaled rarely; the result does not depend on it.
+  if (__any(mx * sc > u.m + kRescale)) {
+    mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+    const float mn = fmaxf(u.m, mx * sc);
+    const float alpha = (mn == u.m) ? 1.0f : __builtin_amdgcn_exp2f(u.m - mn);
     u.l *= alpha;
     u.m = mn;
 #pragma unroll
@@ -304,29 +318,27 @@ __device__ inline void step(Unit<D>& u, const Tile<KIND, D>& T0, const Tile<KIND
     }
   }
 
+  // p = 2^(sc*x - m); masked rows have x = -inf -> p = 0
+  const float mneg = u.m == -INFINITY ? 0.0f : -u.m;
   float pr[8];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    pr[e] = ((va0 >> e) & 1u) ? exp2f(x0[e] - u.m) : 0.f;
-    pr[e + 4] = ((va1 >> e) & 1u) ? exp2f(x1[e] - u.m) : 0.f;
+    pr[e] = __builtin_amdgcn_exp2f(fmaf(x0[e], sc, mneg));
+    pr[e + 4] = __builtin_amdgcn_exp2f(fmaf(x1[e], sc, mneg));
   }
   u.l += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
 
   // A operand of PV: p * v_scale of (position, this row's group), split into
-  // bf16 hi + lo.  Rows outside the context contribute exactly 0.
+  // bf16 hi + lo.  INT8 and bf16 rows carry the 1/16 of the INT4 encoding.
   float ap[8];
   if constexpr (KIND == kBf16Page) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) ap[e] = pr[e] * 0.0625f;
   } else {
-    const float sc = KIND == kInt4Page ? 1.0f : 0.0625f;
     const float sv[8] = {h2f_lo(T0.vs[0]), h2f_hi(T0.vs[0]), h2f_lo(T0.vs[1]), h2f_hi(T0.vs[1]),
                          h2f_lo(T1.vs[0]), h2f_hi(T1.vs[0]), h2f_lo(T1.vs[1]), h2f_hi(T1.vs[1])};
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      ap[e] = ((va0 >> e) & 1u) ? pr[e] * sv[e] * sc : 0.f;
-      ap[e + 4] = ((va1 >> e) & 1u) ? pr[e + 4] * sv[e + 4] * sc : 0.f;
-    }
+    for (int e = 0; e < 8; ++e) ap[e] = KIND == kInt4Page ? pr[e] * sv[e] : pr[e] * (sv[e] * 0.0625f);
   }
   uint32_t hi[4], lo[4];
 #pragma unroll
@@ -347,7 +359,7 @@ __device__ inline void step(Unit<D>& u, const Tile<KIND, D>& T0, const Tile<KIND
   }
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    const bf16x8_t bv = v_operand<KIND, D>(T0, T1, t, va0, va1);
+    const bf16x8_t bv = v_operand<KIND, D>(T0, T1, t);
     f32x4_t c = u.o[t];
     if constexpr (KIND == kInt4Page) {
       c[t / 2] += corr[t / 2];
@@ -359,30 +371,53 @@ __device__ inline void step(Unit<D>& u, const Tile<KIND, D>& T0, const Tile<KIND
   }
 }
 
-// Runs n tiles (ptr(i), mask(i)) two at a time, loading the next pair while
-// computing the current one.  Tile n (odd n) is a masked copy of tile n-1.
-template <int KIND, int D, class PtrFn, class MaskFn>
+// Runs n tiles (ptr(i), mask(i)) two at a time (a step).  STAGES = 1: load
+// then compute; 2: the next step's loads are in flight while a step is
+// computed; 3: the next two steps'.  Tile n (odd n) is a masked copy of n-1.
+template <int KIND, int D, int STAGES, class PtrFn, class MaskFn>
 __device__ inline void run_tiles(Unit<D>& u, int n, PtrFn ptr, MaskFn mask, int lane) {
   if (n <= 0) return;
   const int ln = lane & 15, kg = lane >> 4;
   const int nsteps = (n + 1) >> 1;
-  Tile<KIND, D> a0, a1, b0, b1;
-  a0.load(ptr(0), ln, kg);
-  a1.load(ptr(n > 1 ? 1 : 0), ln, kg);
-  for (int s = 0; s < nsteps; s += 2) {
-    if (s + 1 < nsteps) {
-      const int i = 2 * (s + 1);
-      b0.load(ptr(i), ln, kg);
-      b1.load(ptr(i + 1 < n ? i + 1 : i), ln, kg);
+  auto load = [&](Tile<KIND, D>& t0, Tile<KIND, D>& t1, int s) {
+    const int i = 2 * s;
+    t0.load(ptr(i), ln, kg);
+    t1.load(ptr(i + 1 < n ? i + 1 : i), ln, kg);
+  };
+  auto run = [&](const Tile<KIND, D>& t0, const Tile<KIND, D>& t1, int s) {
+    const int i = 2 * s;
+    step<KIND, D, true>(u, t0, t1, mask(i), i + 1 < n ? mask(i + 1) : 0u, lane);
+  };
+  if constexpr (STAGES == 1) {
+    for (int s = 0; s < nsteps; ++s) {
+      Tile<KIND, D> a0, a1;
+      load(a0, a1, s);
+      run(a0, a1, s);
     }
-    step<KIND, D>(u, a0, a1, mask(2 * s), 2 * s + 1 < n ? mask(2 * s + 1) : 0u, lane);
-    if (s + 1 >= nsteps) break;
-    if (s + 2 < nsteps) {
-      const int i = 2 * (s + 2);
-      a0.load(ptr(i), ln, kg);
-      a1.load(ptr(i + 1 < n ? i + 1 : i), ln, kg);
+  } else if constexpr (STAGES == 2) {
+    Tile<KIND, D> a0, a1, b0, b1;
+    load(a0, a1, 0);
+    for (int s = 0; s < nsteps; s += 2) {
+      if (s + 1 < nsteps) load(b0, b1, s + 1);
+      run(a0, a1, s);
+      if (s + 1 >= nsteps) break;
+      if (s + 2 < nsteps) load(a0, a1, s + 2);
+      run(b0, b1, s + 1);
     }
-    step<KIND, D>(u, b0, b1, mask(2 * s + 2), 2 * s + 3 < n ? mask(2 * s + 3) : 0u, lane);
+  } else {
+    Tile<KIND, D> a0, a1, b0, b1, c0, c1;
+    load(a0, a1, 0);
+    if (nsteps > 1) load(b0, b1, 1);
+    for (int s = 0; s < nsteps; s += 3) {
+      if (s + 2 < nsteps) load(c0, c1, s + 2);
+      run(a0, a1, s);
+      if (s + 1 >= nsteps) break;
+      if (s + 3 < nsteps) load(a0, a1, s + 3);
+      run(b0, b1, s + 1);
+      if (s + 2 >= nsteps) break;
+      if (s + 4 < nsteps) load(b0, b1, s + 4);
+      run(c0, c1, s + 2);
+    }
   }
 }
 
@@ -394,29 +429,95 @@ __device__ inline uint32_t range_mask(int lo, int hi) {  // bits [lo, hi) of 0..
 }
 
 // ---------------------------------------------------------------- worklist --
-__device__ inline int items_of(int L, int S, int R, int chunk_pages) {
-  const Regions g = regions(L, S, R);
-  int np = 0;
-  if (g.me > g.mb) np = (g.me - 1) / kPage - g.mb / kPage + 1;
-  const int n = (np + chunk_pages - 1) / chunk_pages;
+constexpr int kMaxChunkPages = 255;  // item cost buckets of the longest-first order
+constexpr int kProtectedCost = 2;    // an INT8 tile costs about two INT4 pages
+
+struct SeqWork {
+  int L;          // context length (clamped to the page table)
+  int mid_first;  // first / last page holding middle rows (last < first: none)
+  int mid_last;
+  int prot_tiles;  // INT8 side tiles holding protected rows
+};
+
+__device__ inline SeqWork seq_work(const DecodeParams& p, int b) {
+  SeqWork w;
+  int L = p.seq_lens[b];
+  L = L < 0 ? 0 : (L > p.max_pages * kPage ? p.max_pages * kPage : L);
+  w.L = L;
+  const Regions g = regions(L, p.n_sink, p.n_recent);
+  w.mid_first = g.mb / kPage;
+  w.mid_last = g.me > g.mb ? (g.me - 1) / kPage : w.mid_first - 1;
+  const int S = p.n_sink, R = p.n_recent;
+  const int se = L < S ? L : S;
+  const int nring = L > S ? (L - S < R ? L - S : R) : 0;
+  const int rows = nring > 0 ? S + nring : se;
+  w.prot_tiles = (rows + kPage - 1) / kPage;
+  return w;
+}
+
+__device__ inline int n_items(const SeqWork& w, int chunk) {
+  const int np = w.mid_last - w.mid_first + 1;
+  const int n = (np + chunk - 1) / chunk;
   return n < 1 ? 1 : n;
 }
 
-__global__ __launch_bounds__(1024) void worklist_kernel(DecodeParams p) {
-  __shared__ int scan[1024];
+__device__ inline int item_cost(const SeqWork& w, int chunk, int k) {
+  const int np = w.mid_last - w.mid_first + 1;
+  int pages = np - k * chunk;
+  pages = pages > chunk ? chunk : (pages < 0 ? 0 : pages);
+  const int c = 1 + pages + (k == 0 ? kProtectedCost * w.prot_tiles : 0);
+  return c > kMaxChunkPages ? kMaxChunkPages : c;
+}
+
+// One workgroup: chooses the chunk size from the total work, numbers the
+// partial slots of split sequences, and lists the items longest first (a
+// counting sort over item cost) so that the dynamic schedule ends on small
+// items.
+__global__ __launch_bounds__(1024) void worklist_kernel(DecodeParams p, int units_per_item) {
+  __shared__ unsigned long long total_pages;
+  __shared__ int chunk_sh;
   __shared__ int running;
+  __shared__ uint32_t nmerge;
+  __shared__ int scan[1024];
+  __shared__ uint32_t bucket[kMaxChunkPages + 1];
   const int tid = threadIdx.x;
-  if (tid == 0) running = 0;
+  if (tid == 0) {
+    total_pages = 0ull;
+    running = 0;
+    nmerge = 0u;
+  }
+  for (int i = tid; i <= kMaxChunkPages; i += 1024) bucket[i] = 0u;
   __syncthreads();
+  unsigned long long mine = 0ull;
+  for (int b = tid; b < p.batch; b += 1024) {
+    const SeqWork w = seq_work(p, b);
+    mine += unsigned(w.mid_last - w.mid_first + 1) + unsigned(kProtectedCost * w.prot_tiles);
+  }
+  atomicAdd(&total_pages, mine);
+  __syncthreads();
+  if (tid == 0) {
+    // about 8 units per resident wave
+    const unsigned long long denom = 8ull * unsigned(p.resident_waves > 0 ? p.resident_waves : 1);
+    unsigned long long c = (total_pages * unsigned(units_per_item) + denom - 1) / denom;
+    c = c < unsigned(kChunkPages) ? unsigned(kChunkPages) : (c > unsigned(kMaxChunkPages) ? kMaxChunkPages : c);
+    chunk_sh = int(c);
+  }
+  __syncthreads();
+  const int chunk = chunk_sh;
+
+  // partial slots (prefix over split sequences) and the cost histogram
   for (int base = 0; base < p.batch; base += 1024) {
     const int b = base + tid;
-    int n = 0;
+    int n = 0, split = 0;
+    SeqWork w{};
     if (b < p.batch) {
-      int L = p.seq_lens[b];
-      L = L < 0 ? 0 : (L > p.max_pages * kPage ? p.max_pages * kPage : L);
-      n = items_of(L, p.n_sink, p.n_recent, p.chunk_pages);
+      w = seq_work(p, b);
+      n = n_items(w, chunk);
+      split = n > 1 ? n : 0;
+      for (int k = 0; k < n; ++k) atomicAdd(&bucket[kMaxChunkPages - item_cost(w, chunk, k)], 1u);
+      if (n > 1) p.ws.merge_list[atomicAdd(&nmerge, 1u)] = b;
     }
-    scan[tid] = n;
+    scan[tid] = split;
     __syncthreads();
     for (int o = 1; o < 1024; o <<= 1) {  // inclusive Hillis-Steele scan
       const int v = tid >= o ? scan[tid - o] : 0;
@@ -424,25 +525,43 @@ __global__ __launch_bounds__(1024) void worklist_kernel(DecodeParams p) {
       scan[tid] += v;
       __syncthreads();
     }
-    const int start = running + scan[tid] - n;
     if (b < p.batch) {
-      p.ws.item_base[b] = start;
+      p.ws.item_base[b] = running + scan[tid] - split;
       p.ws.item_count[b] = n;
-      for (int k = 0; k < n; ++k) p.ws.items[start + k] = make_int2(b, k);
     }
     __syncthreads();
     if (tid == 1023) running += scan[1023];
     __syncthreads();
   }
+  // bucket offsets (descending cost) ...
   if (tid == 0) {
+    uint32_t acc = 0u;
+    for (int i = 0; i <= kMaxChunkPages; ++i) {
+      const uint32_t c = bucket[i];
+      bucket[i] = acc;
+      acc += c;
+    }
     p.ws.header[0] = 0u;
-    p.ws.header[1] = uint32_t(running);
+    p.ws.header[1] = acc;
+    p.ws.header[2] = uint32_t(chunk);
+    p.ws.header[3] = nmerge;
+  }
+  __syncthreads();
+  // ... and the scatter
+  for (int b = tid; b < p.batch; b += 1024) {
+    const SeqWork w = seq_work(p, b);
+    const int n = n_items(w, chunk);
+    for (int k = 0; k < n; ++k) {
+      const uint32_t pos = atomicAdd(&bucket[kMaxChunkPages - item_cost(w, chunk, k)], 1u);
+      p.ws.items[pos] = make_int2(b, k);
+    }
   }
 }
 
 // ------------------------------------------------------------- attention --
 template <int FMT, int D>
-__global__ __launch_bounds__(256) void attention_kernel(DecodeParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KV4_WAVES_PER_EU, 8))) void attention_kernel(
+    DecodeParams p) {
   constexpr int NG = D / 32, HB = 16 / NG, NT = D / 16;
   constexpr int MAIN = FMT == kFmtKV4 ? kInt4Page : (FMT == kFmtKV8 ? kInt8Tile : kBf16Page);
   const int lane = threadIdx.x & (kWave - 1);
@@ -452,17 +571,19 @@ __global__ __launch_bounds__(256) void attention_kernel(DecodeParams p) {
   const int S = FMT == kFmtKV4 ? p.n_sink : 0;
   const int R = FMT == kFmtKV4 ? p.n_recent : 0;
   const int64_t units = int64_t(p.ws.header[1]) * H * NHB;
+  const int chunk = int(p.ws.header[2]);
 
-  for (;;) {
-    int ui = 0;
-    if (lane == 0) ui = int(atomicAdd(&p.ws.header[0], 1u));
-    const int64_t uu = __shfl(ui, 0, kWave);
-    if (uu >= units) break;
+  uint32_t nxt = 0;
+  if (lane == 0) nxt = atomicAdd(&p.ws.header[0], 1u);
+  int64_t uu = __builtin_amdgcn_readfirstlane(nxt);
+  while (uu < units) {
+    // fetch the next unit now; the atomic's latency hides behind this one
+    if (lane == 0) nxt = atomicAdd(&p.ws.header[0], 1u);
     const int64_t item = uu / (H * NHB);
     const int rem = int(uu % (H * NHB));
     const int h = rem / NHB, hb = rem % NHB;
     const int2 it = p.ws.items[item];
-    const int b = it.x, chunk = it.y;
+    const int b = it.x, ck = it.y;
     int L = p.seq_lens[b];
     L = L < 0 ? 0 : (L > p.max_pages * kPage ? p.max_pages * kPage : L);
     const Regions g = regions(L, S, R);
@@ -492,8 +613,14 @@ __global__ __launch_bounds__(256) void attention_kernel(DecodeParams p) {
       }
       double qs = 0.0;
       if (MAIN == kInt4Page && valid) {
+        const uint4* qg = reinterpret_cast<const uint4*>(qrow + grp * 32);
 #pragma unroll
-        for (int c = 0; c < 32; ++c) qs += double(bf16_to_f32(qrow[grp * 32 + c]));
+        for (int i = 0; i < 4; ++i) {
+          const uint4 a = qg[i];
+          const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+          for (int k = 0; k < 4; ++k) qs += double(bf16_lo(w[k])) + double(bf16_hi(w[k]));
+        }
       }
       u.qsum = float(qs);
 #pragma unroll
@@ -504,7 +631,7 @@ __global__ __launch_bounds__(256) void attention_kernel(DecodeParams p) {
     }
 
     // ---- protected rows: INT8 side-cache tiles (sinks, then the ring)
-    if (FMT == kFmtKV4 && chunk == 0 && L > 0 && S + R > 0) {
+    if (FMT == kFmtKV4 && ck == 0 && L > 0 && S + R > 0) {
       const int slot = p.slot_ids ? p.slot_ids[b] : b;
       if (slot >= 0 && slot < p.num_slots) {
         const int se = L < S ? L : S;
@@ -517,31 +644,33 @@ __global__ __launch_bounds__(256) void attention_kernel(DecodeParams p) {
           const int r0 = i * kPage;
           return range_mask(0 - r0, se - r0) | range_mask(S - r0, S + nring - r0);
         };
-        run_tiles<kInt8Tile, D>(u, ntiles, ptr, mask, lane);
+        run_tiles<kInt8Tile, D, KV4_STAGES8>(u, ntiles, ptr, mask, lane);
       }
     }
 
-    // ---- middle pages of this chunk
+    // ---- middle pages of this item, page ids fetched 64 at a time
     if (g.me > g.mb) {
-      const int first = g.mb / kPage + chunk * p.chunk_pages;
-      int last = first + p.chunk_pages - 1;
+      const int first = g.mb / kPage + ck * chunk;
+      int last = first + chunk - 1;
       if (last > (g.me - 1) / kPage) last = (g.me - 1) / kPage;
-      const int npg = last - first + 1;
-      int pid_l = 0;
-      if (lane < npg) {
-        const int64_t v = p.page_table[int64_t(b) * p.max_pages + first + lane];
-        pid_l = (v < 0 || v >= p.num_pages) ? -1 : int(v);
+      for (int base = first; base <= last; base += kWave) {
+        const int npg = (last - base + 1) < kWave ? (last - base + 1) : kWave;
+        int pid_l = 0;
+        if (lane < npg) {
+          const int64_t v = p.page_table[int64_t(b) * p.max_pages + base + lane];
+          pid_l = (v < 0 || v >= p.num_pages) ? -1 : int(v);
+        }
+        auto ptr = [&](int i) {
+          const int pid = __builtin_amdgcn_readlane(pid_l, i);
+          return p.pages + (int64_t(pid < 0 ? 0 : pid) * H + h) * p.block_bytes;
+        };
+        auto mask = [&](int i) {
+          const int pid = __builtin_amdgcn_readlane(pid_l, i);
+          const int p0 = (base + i) * kPage;
+          return pid < 0 ? 0u : range_mask(g.mb - p0, g.me - p0);
+        };
+        run_tiles<MAIN, D, MAIN == kInt4Page ? KV4_STAGES : (MAIN == kInt8Tile ? KV4_STAGES8 : 1)>(u, npg, ptr, mask, lane);
       }
-      auto ptr = [&](int i) {
-        const int pid = __builtin_amdgcn_readlane(pid_l, i);
-        return p.pages + (int64_t(pid < 0 ? 0 : pid) * H + h) * p.block_bytes;
-      };
-      auto mask = [&](int i) {
-        const int pid = __builtin_amdgcn_readlane(pid_l, i);
-        const int p0 = (first + i) * kPage;
-        return pid < 0 ? 0u : range_mask(g.mb - p0, g.me - p0);
-      };
-      run_tiles<MAIN, D>(u, npg, ptr, mask, lane);
     }
 
     // ---- finish: per-head denominators, then output or partial
@@ -549,6 +678,7 @@ __global__ __launch_bounds__(256) void attention_kernel(DecodeParams p) {
     lt += __shfl_xor(lt, 16, kWave);
     lt += __shfl_xor(lt, 32, kWave);
     const int nitems = p.ws.item_count[b];
+    const int64_t pslot = int64_t(p.ws.item_base[b]) + ck;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
 #pragma unroll
@@ -564,7 +694,7 @@ __global__ __launch_bounds__(256) void attention_kernel(DecodeParams p) {
             const float v = lh > 0.f ? 16.0f * u.o[t][e] / lh : 0.f;
             p.out[(int64_t(b) * Hq + hq) * D + c] = f32_to_bf16_bits(v);
           } else {
-            p.ws.partials[((int64_t(p.ws.item_base[b]) + chunk) * Hq + hq) * (D + 2) + c] = 16.0f * u.o[t][e];
+            p.ws.partials[(pslot * Hq + hq) * (D + 2) + c] = 16.0f * u.o[t][e];
           }
         }
       }
@@ -576,77 +706,88 @@ __global__ __launch_bounds__(256) void attention_kernel(DecodeParams p) {
         if (nitems == 1) {
           if (p.lse) p.lse[int64_t(b) * Hq + hq] = lt > 0.f ? (u.m + log2f(lt)) * kLn2 : -INFINITY;
         } else {
-          float* part = p.ws.partials + ((int64_t(p.ws.item_base[b]) + chunk) * Hq + hq) * (D + 2);
+          float* part = p.ws.partials + (pslot * Hq + hq) * (D + 2);
           part[D] = u.m;
           part[D + 1] = lt;
         }
       }
     }
+    uu = __builtin_amdgcn_readfirstlane(nxt);
   }
 }
 
 // ----------------------------------------------------------------- merge ---
+// Exact log-sum-exp merge of the partials of split sequences; a persistent
+// grid strides over (split sequence, query head) pairs.
 template <int D>
 __global__ __launch_bounds__(256) void merge_kernel(DecodeParams p) {
   constexpr int E = D / kWave;
   const int lane = threadIdx.x & (kWave - 1);
   const int Hq = p.num_q_heads;
-  const int64_t w = int64_t(blockIdx.x) * (blockDim.x / kWave) + threadIdx.x / kWave;
-  if (w >= int64_t(p.batch) * Hq) return;
-  const int b = int(w / Hq), hq = int(w % Hq);
-  const int n = p.ws.item_count[b];
-  if (n <= 1) return;
-  const int64_t base = int64_t(p.ws.item_base[b]) * Hq + hq;
-  float M = -INFINITY;
-  for (int i = 0; i < n; ++i) {
-    const float* part = p.ws.partials + (base + int64_t(i) * Hq) * (D + 2);
-    if (part[D + 1] > 0.f) M = fmaxf(M, part[D]);
+  const int64_t nw = int64_t(gridDim.x) * (blockDim.x / kWave);
+  const int64_t tasks = int64_t(p.ws.header[3]) * Hq;
+  for (int64_t w = int64_t(blockIdx.x) * (blockDim.x / kWave) + threadIdx.x / kWave; w < tasks; w += nw) {
+    const int b = p.ws.merge_list[w / Hq], hq = int(w % Hq);
+    const int n = p.ws.item_count[b];
+    const int64_t base = int64_t(p.ws.item_base[b]) * Hq + hq;
+    float M = -INFINITY;
+    for (int i = 0; i < n; ++i) {
+      const float* part = p.ws.partials + (base + int64_t(i) * Hq) * (D + 2);
+      if (part[D + 1] > 0.f) M = fmaxf(M, part[D]);
+    }
+    float l = 0.f, o[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) o[e] = 0.f;
+    for (int i = 0; i < n; ++i) {
+      const float* part = p.ws.partials + (base + int64_t(i) * Hq) * (D + 2);
+      const float li = part[D + 1];
+      if (!(li > 0.f)) continue;  // an item without context rows
+      const float a = __builtin_amdgcn_exp2f(part[D] - M);
+      l += a * li;
+#pragma unroll
+      for (int e = 0; e < E; ++e) o[e] = fmaf(a, part[lane * E + e], o[e]);
+    }
+    const float inv = l > 0.f ? 1.0f / l : 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) p.out[(int64_t(b) * Hq + hq) * D + lane * E + e] = f32_to_bf16_bits(o[e] * inv);
+    if (p.lse && lane == 0) p.lse[int64_t(b) * Hq + hq] = l > 0.f ? (M + log2f(l)) * kLn2 : -INFINITY;
   }
-  float l = 0.f, o[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) o[e] = 0.f;
-  for (int i = 0; i < n; ++i) {
-    const float* part = p.ws.partials + (base + int64_t(i) * Hq) * (D + 2);
-    const float li = part[D + 1];
-    if (!(li > 0.f)) continue;  // an item without context rows
-    const float a = exp2f(part[D] - M);
-    l += a * li;
-#pragma unroll
-    for (int e = 0; e < E; ++e) o[e] = fmaf(a, part[lane * E + e], o[e]);
-  }
-  const float inv = l > 0.f ? 1.0f / l : 0.f;
-#pragma unroll
-  for (int e = 0; e < E; ++e) p.out[(int64_t(b) * Hq + hq) * D + lane * E + e] = f32_to_bf16_bits(o[e] * inv);
-  if (p.lse && lane == 0) p.lse[int64_t(b) * Hq + hq] = l > 0.f ? (M + log2f(l)) * kLn2 : -INFINITY;
 }
 
 // --------------------------------------------------------------- launch ---
 template <class K>
-int persistent_blocks(K kernel) {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 0;
-  int cus = 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+int blocks_per_cu(K kernel) {
   int per_cu = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(kernel), 256, 0) !=
           hipSuccess ||
       per_cu < 1)
     per_cu = 1;
-  return cus * per_cu;
+  return per_cu;
+}
+
+int device_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  return cus;
 }
 
 template <int FMT, int D>
-hipError_t launch_fd(const DecodeParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL(worklist_kernel, dim3(1), dim3(1024), 0, stream, p);
+hipError_t launch_fd(DecodeParams p, hipStream_t stream) {
+  constexpr int HB = 16 / (D / 32);
+  const int cus = device_cus();
+  if (cus <= 0) return hipErrorInvalidDevice;
+  const int blocks = cus * blocks_per_cu(attention_kernel<FMT, D>);
+  p.resident_waves = blocks * 4;
+  const int G = p.num_q_heads / p.num_kv_heads;
+  const int units_per_item = p.num_kv_heads * ((G + HB - 1) / HB);
+  hipLaunchKernelGGL(worklist_kernel, dim3(1), dim3(1024), 0, stream, p, units_per_item);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const int blocks = persistent_blocks(attention_kernel<FMT, D>);
-  if (blocks <= 0) return hipErrorInvalidDevice;
   hipLaunchKernelGGL((attention_kernel<FMT, D>), dim3(blocks), dim3(256), 0, stream, p);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const int64_t waves = int64_t(p.batch) * p.num_q_heads;
-  hipLaunchKernelGGL((merge_kernel<D>), dim3(unsigned((waves + 3) / 4)), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((merge_kernel<D>), dim3(cus * 2), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -657,7 +798,6 @@ hipError_t launch_fmt(const DecodeParams& p, int head_dim, hipStream_t stream) {
 
 }  // namespace
 
-int32_t decode_chunk_pages() { return kChunkPages; }
 
 static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -669,8 +809,7 @@ static int64_t max_items_of(int32_t batch, int32_t max_pages) {
 size_t decode_workspace_bytes(int32_t batch, int32_t max_pages, int32_t num_q_heads, int32_t head_dim) {
   const int64_t max_items = max_items_of(batch, max_pages);
   size_t s = 256;                                   // header
-  s += align256(sizeof(int32_t) * size_t(batch));  // item_base
-  s += align256(sizeof(int32_t) * size_t(batch));  // item_count
+  s += 3 * align256(sizeof(int32_t) * size_t(batch));  // item_base, item_count, merge_list
   s += align256(sizeof(int2) * size_t(max_items)); // items
   s += align256(sizeof(float) * size_t(max_items) * num_q_heads * (head_dim + 2));
   return s;
@@ -688,6 +827,8 @@ DecodeWorkspace carve_workspace(void* base, int32_t batch, int32_t max_pages, in
   w.item_base = reinterpret_cast<int32_t*>(q);
   q += align256(sizeof(int32_t) * size_t(batch));
   w.item_count = reinterpret_cast<int32_t*>(q);
+  q += align256(sizeof(int32_t) * size_t(batch));
+  w.merge_list = reinterpret_cast<int32_t*>(q);
   q += align256(sizeof(int32_t) * size_t(batch));
   w.items = reinterpret_cast<int2*>(q);
   q += align256(sizeof(int2) * size_t(max_items));

@@ -26,11 +26,13 @@ __host__ __device__ constexpr int side_tiles(int S, int R) { return (S + R + kPa
 // ---- INT4 page block (r = row, c = channel) ----------------------------------
 // K codes: row-major nibbles, even channel in the low nibble.
 __host__ __device__ constexpr size_t k4_byte(int D, int r, int c) { return size_t(r) * (D / 2) + c / 2; }
-// V codes: tiled so that the 4 positions of a row quad and 8 (D=128) channels
-// n, n+16, ... sit in one contiguous D/8-byte run; a byte holds channels c
-// and c+16 (t even in the low nibble) of one position.
+// V codes: tiled so that the 4 positions of a row quad and the D/16 channels
+// n, n+16, ... sit in one contiguous D/8-byte run.  A 32-bit word holds 4 of
+// those channels for positions rr (low half) and rr+1 (high half); a byte
+// holds channels c and c+16 (c/16 even in the low nibble) of one position.
 __host__ __device__ constexpr size_t v4_byte(int D, int r, int c) {
-  return size_t(8) * D + size_t((r / 4) * 16 + c % 16) * (D / 8) + (r % 4) * (D / 32) + (c / 16) / 2;
+  return size_t(8) * D + size_t((r / 4) * 16 + c % 16) * (D / 8) +
+         4 * (((r % 4) / 2) * (D / 64) + (c / 16) / 4) + 2 * ((r % 4) % 2) + ((c / 16) % 4) / 2;
 }
 __host__ __device__ constexpr size_t k4_scale(int D, int r, int grp) { return size_t(16) * D + (grp * 16 + r) * 2; }
 __host__ __device__ constexpr size_t v4_scale(int D, int r, int grp) { return size_t(17) * D + (grp * 16 + r) * 2; }

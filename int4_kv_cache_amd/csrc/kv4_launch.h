@@ -29,13 +29,15 @@ struct AppendParams {
 
 hipError_t launch_append(int fmt, const AppendParams& p, int head_dim, hipStream_t stream);
 
-// Decode workspace: a header, the per-sequence item table, the work items and
-// the fp32 partial results of sequences split over several items.
+// Decode workspace: a header, per-sequence item table, the work items
+// (longest first), the list of sequences split over several items and the
+// fp32 partial results of those items.
 struct DecodeWorkspace {
-  uint32_t* header;      // [0] unit counter, [1] total items
-  int32_t* item_base;    // [batch]
+  uint32_t* header;      // [0] unit counter, [1] items, [2] chunk pages, [3] split sequences
+  int32_t* item_base;    // [batch] first partial slot of a split sequence
   int32_t* item_count;   // [batch]
-  int2* items;           // [max_items] (sequence, chunk)
+  int32_t* merge_list;   // [batch] split sequences
+  int2* items;           // [max_items] (sequence, chunk index)
   float* partials;       // [max_items][num_q_heads][head_dim + 2]
   int64_t max_items;
 };
@@ -60,11 +62,10 @@ struct DecodeParams {
   int32_t n_recent;
   int64_t block_bytes;
   int64_t side_bytes;
-  int32_t chunk_pages;
+  int32_t resident_waves;  // attention waves resident on the device at once
   DecodeWorkspace ws;
 };
 
-int32_t decode_chunk_pages();
 size_t decode_workspace_bytes(int32_t batch, int32_t max_pages, int32_t num_q_heads, int32_t head_dim);
 DecodeWorkspace carve_workspace(void* base, int32_t batch, int32_t max_pages, int32_t num_q_heads,
                                 int32_t head_dim);

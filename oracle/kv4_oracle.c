@@ -116,8 +116,10 @@ void orc_quant_sym(const uint16_t* x_bf16, int n, int qmax, int8_t* codes,
  *
  *   INT4 page block, 18*D bytes:
  *     K codes   [0, 8D)    byte r*(D/2) + c/2; low nibble = even channel
- *     V codes   [8D, 16D)  byte (q4*16 + n)*(D/8) + rr*(D/32) + t/2;
- *                          low nibble = even t
+ *     V codes   [8D, 16D)  byte (q4*16 + n)*(D/8) + 4*((rr/2)*(D/64) + t/4)
+ *                          + 2*(rr%2) + (t%4)/2; low nibble = even t
+ *                          (a 32-bit word holds 4 channels of positions
+ *                          rr and rr+1 of a row quad, one 16-bit half each)
  *     K scales  [16D, 17D) fp16 at (grp*16 + r)*2, grp = c / 32
  *     V scales  [17D, 18D) fp16 likewise
  *   Nibbles hold the code in two's complement.
@@ -160,7 +162,8 @@ static size_t k4_byte(int D, int r, int c) { return (size_t)r * (D / 2) + c / 2;
 static int k4_high(int c) { return c & 1; }
 static size_t v4_byte(int D, int r, int c) {
   int q4 = r / 4, rr = r % 4, t = c / 16, n = c % 16;
-  return (size_t)8 * D + (size_t)(q4 * 16 + n) * (D / 8) + rr * (D / 32) + t / 2;
+  int word = (rr / 2) * (D / 64) + t / 4;
+  return (size_t)8 * D + (size_t)(q4 * 16 + n) * (D / 8) + 4 * word + 2 * (rr % 2) + (t % 4) / 2;
 }
 static int v4_high(int c) { return (c / 16) & 1; }
 static size_t k4_scale(int D, int r, int c) { return (size_t)16 * D + ((c / 32) * 16 + r) * 2; }

@@ -99,6 +99,10 @@ def test_host_argument_errors_return_before_launch(lib):
     assert _call_decode(lib, good, kv4.CacheDesc(None, 10, fake, 4), batch) == -1
     assert _call_decode(lib, good, cache, kv4.BatchDesc(None, 4, fake, None, 4)) == -1
     assert _call_decode(lib, good, cache, kv4.BatchDesc(fake, 0, fake, None, 4)) == -1
+    # softmax scale must be positive and finite
+    for sm in (0.0, -1.0, float("inf"), float("nan")):
+        assert lib.kv4_decode_attention(ctypes.byref(good), ctypes.byref(cache), ctypes.byref(batch), fake,
+                                        sm, fake, None, fake, 1 << 40, None) == -1
     # workspace too small
     assert _call_decode(lib, good, cache, batch, ws_bytes=16) == -3
     # append argument errors
