@@ -373,13 +373,18 @@ __device__ inline void step(Unit<D>& u, const Tile<KIND, D>& T0, const Tile<KIND
 
 // Runs n tiles (ptr(i), mask(i)) two at a time (a step).  STAGES = 1: load
 // then compute; 2: the next step's loads are in flight while a step is
-// computed; 3: the next two steps'.  Tile n (odd n) is a masked copy of n-1.
+// computed; 3: the next two steps'.  Every load is issued unconditionally
+// (past the end it re-reads the last step, which the L2 holds) so the loop
+// body has one fixed load sequence and each wait covers exactly the step it
+// needs.  Tile n (odd n) is a masked copy of tile n-1.
 template <int KIND, int D, int STAGES, class PtrFn, class MaskFn>
 __device__ inline void run_tiles(Unit<D>& u, int n, PtrFn ptr, MaskFn mask, int lane) {
   if (n <= 0) return;
   const int ln = lane & 15, kg = lane >> 4;
   const int nsteps = (n + 1) >> 1;
+  const int last = nsteps - 1;
   auto load = [&](Tile<KIND, D>& t0, Tile<KIND, D>& t1, int s) {
+    s = s < last ? s : last;
     const int i = 2 * s;
     t0.load(ptr(i), ln, kg);
     t1.load(ptr(i + 1 < n ? i + 1 : i), ln, kg);
@@ -397,26 +402,28 @@ __device__ inline void run_tiles(Unit<D>& u, int n, PtrFn ptr, MaskFn mask, int 
   } else if constexpr (STAGES == 2) {
     Tile<KIND, D> a0, a1, b0, b1;
     load(a0, a1, 0);
-    for (int s = 0; s < nsteps; s += 2) {
-      if (s + 1 < nsteps) load(b0, b1, s + 1);
+    for (int s = 0;; s += 2) {
+      load(b0, b1, s + 1);
       run(a0, a1, s);
       if (s + 1 >= nsteps) break;
-      if (s + 2 < nsteps) load(a0, a1, s + 2);
+      load(a0, a1, s + 2);
       run(b0, b1, s + 1);
+      if (s + 2 >= nsteps) break;
     }
   } else {
     Tile<KIND, D> a0, a1, b0, b1, c0, c1;
     load(a0, a1, 0);
-    if (nsteps > 1) load(b0, b1, 1);
-    for (int s = 0; s < nsteps; s += 3) {
-      if (s + 2 < nsteps) load(c0, c1, s + 2);
+    load(b0, b1, 1);
+    for (int s = 0;; s += 3) {
+      load(c0, c1, s + 2);
       run(a0, a1, s);
       if (s + 1 >= nsteps) break;
-      if (s + 3 < nsteps) load(a0, a1, s + 3);
+      load(a0, a1, s + 3);
       run(b0, b1, s + 1);
       if (s + 2 >= nsteps) break;
-      if (s + 4 < nsteps) load(b0, b1, s + 4);
+      load(b0, b1, s + 4);
       run(c0, c1, s + 2);
+      if (s + 3 >= nsteps) break;
     }
   }
 }
@@ -429,12 +436,12 @@ __device__ inline uint32_t range_mask(int lo, int hi) {  // bits [lo, hi) of 0..
 }
 
 // ---------------------------------------------------------------- worklist --
-constexpr int kMaxChunkPages = 255;  // item cost buckets of the longest-first order
+constexpr int kMaxChunkPages = 64;  // one lane per page id of an item
 constexpr int kProtectedCost = 2;    // an INT8 tile costs about two INT4 pages
 
 struct SeqWork {
-  int L;          // context length (clamped to the page table)
-  int mid_first;  // first / last page holding middle rows (last < first: none)
+  int L;           // context length (clamped to the page table)
+  int mid_first;   // first / last page holding middle rows (last < first: none)
   int mid_last;
   int prot_tiles;  // INT8 side tiles holding protected rows
 };
@@ -455,43 +462,50 @@ __device__ inline SeqWork seq_work(const DecodeParams& p, int b) {
   return w;
 }
 
+__device__ inline int mid_pages(const SeqWork& w) { return w.mid_last - w.mid_first + 1; }
 __device__ inline int n_items(const SeqWork& w, int chunk) {
-  const int np = w.mid_last - w.mid_first + 1;
-  const int n = (np + chunk - 1) / chunk;
+  const int n = (mid_pages(w) + chunk - 1) / chunk;
   return n < 1 ? 1 : n;
 }
+__device__ inline int item_pages(const SeqWork& w, int chunk, int k) {
+  const int r = mid_pages(w) - k * chunk;
+  return r > chunk ? chunk : (r < 0 ? 0 : r);
+}
 
-__device__ inline int item_cost(const SeqWork& w, int chunk, int k) {
-  const int np = w.mid_last - w.mid_first + 1;
-  int pages = np - k * chunk;
-  pages = pages > chunk ? chunk : (pages < 0 ? 0 : pages);
-  const int c = 1 + pages + (k == 0 ? kProtectedCost * w.prot_tiles : 0);
-  return c > kMaxChunkPages ? kMaxChunkPages : c;
+// Work-item descriptor, two int4:
+//   [0] = {b, L, first middle page of the item, (chunk index << 8) | pages}
+//   [1] = {items of b, first partial slot of b, side slot, 0}
+__device__ inline void write_item(const DecodeParams& p, uint32_t pos, int b, const SeqWork& w, int chunk, int k,
+                                  int n, int pbase) {
+  const int slot = p.slot_ids ? p.slot_ids[b] : b;
+  p.ws.items[2 * pos] = make_int4(b, w.L, w.mid_first + k * chunk, (k << 8) | item_pages(w, chunk, k));
+  p.ws.items[2 * pos + 1] = make_int4(n, pbase, slot, 0);
 }
 
 // One workgroup: chooses the chunk size from the total work, numbers the
-// partial slots of split sequences, and lists the items longest first (a
-// counting sort over item cost) so that the dynamic schedule ends on small
-// items.
+// partial slots of split sequences and writes the item descriptors: all full
+// chunks first, then the remaining (shorter) items in decreasing size, so the
+// dynamic schedule ends on small items.
 __global__ __launch_bounds__(1024) void worklist_kernel(DecodeParams p, int units_per_item) {
   __shared__ unsigned long long total_pages;
   __shared__ int chunk_sh;
-  __shared__ int running;
+  __shared__ int run_full, run_split;
   __shared__ uint32_t nmerge;
-  __shared__ int scan[1024];
-  __shared__ uint32_t bucket[kMaxChunkPages + 1];
+  __shared__ unsigned long long scan[1024];  // (split items << 32) | full items
+  __shared__ uint32_t bucket[kMaxChunkPages + 2];
   const int tid = threadIdx.x;
   if (tid == 0) {
     total_pages = 0ull;
-    running = 0;
+    run_full = 0;
+    run_split = 0;
     nmerge = 0u;
   }
-  for (int i = tid; i <= kMaxChunkPages; i += 1024) bucket[i] = 0u;
+  for (int i = tid; i < kMaxChunkPages + 2; i += 1024) bucket[i] = 0u;
   __syncthreads();
   unsigned long long mine = 0ull;
   for (int b = tid; b < p.batch; b += 1024) {
     const SeqWork w = seq_work(p, b);
-    mine += unsigned(w.mid_last - w.mid_first + 1) + unsigned(kProtectedCost * w.prot_tiles);
+    mine += unsigned(mid_pages(w)) + unsigned(kProtectedCost * w.prot_tiles);
   }
   atomicAdd(&total_pages, mine);
   __syncthreads();
@@ -505,37 +519,43 @@ __global__ __launch_bounds__(1024) void worklist_kernel(DecodeParams p, int unit
   __syncthreads();
   const int chunk = chunk_sh;
 
-  // partial slots (prefix over split sequences) and the cost histogram
+  // pass 1: full items (scan) and the histogram of the other items' sizes
   for (int base = 0; base < p.batch; base += 1024) {
     const int b = base + tid;
-    int n = 0, split = 0;
-    SeqWork w{};
+    int full = 0, split = 0;
     if (b < p.batch) {
-      w = seq_work(p, b);
-      n = n_items(w, chunk);
+      const SeqWork w = seq_work(p, b);
+      const int n = n_items(w, chunk);
+      for (int k = 0; k < n; ++k) {
+        const int pg = item_pages(w, chunk, k);
+        if (pg == chunk) ++full;
+        else atomicAdd(&bucket[kMaxChunkPages - pg], 1u);
+      }
       split = n > 1 ? n : 0;
-      for (int k = 0; k < n; ++k) atomicAdd(&bucket[kMaxChunkPages - item_cost(w, chunk, k)], 1u);
-      if (n > 1) p.ws.merge_list[atomicAdd(&nmerge, 1u)] = b;
     }
-    scan[tid] = split;
+    const unsigned long long mine2 = (unsigned long long)full | ((unsigned long long)split << 32);
+    scan[tid] = mine2;
     __syncthreads();
-    for (int o = 1; o < 1024; o <<= 1) {  // inclusive Hillis-Steele scan
-      const int v = tid >= o ? scan[tid - o] : 0;
+    for (int o = 1; o < 1024; o <<= 1) {  // inclusive Hillis-Steele scan of two 32-bit counts
+      const unsigned long long v = tid >= o ? scan[tid - o] : 0ull;
       __syncthreads();
       scan[tid] += v;
       __syncthreads();
     }
     if (b < p.batch) {
-      p.ws.item_base[b] = running + scan[tid] - split;
-      p.ws.item_count[b] = n;
+      const unsigned long long ex = scan[tid] - mine2;
+      p.ws.item_base[b] = run_split + int(ex >> 32);
+      p.ws.merge_list[b] = run_full + int(ex & 0xFFFFFFFFull);  // scratch: first full-item position
     }
     __syncthreads();
-    if (tid == 1023) running += scan[1023];
+    if (tid == 1023) {
+      run_full += int(scan[1023] & 0xFFFFFFFFull);
+      run_split += int(scan[1023] >> 32);
+    }
     __syncthreads();
   }
-  // bucket offsets (descending cost) ...
   if (tid == 0) {
-    uint32_t acc = 0u;
+    uint32_t acc = uint32_t(run_full);  // shorter items follow the full ones
     for (int i = 0; i <= kMaxChunkPages; ++i) {
       const uint32_t c = bucket[i];
       bucket[i] = acc;
@@ -544,21 +564,49 @@ __global__ __launch_bounds__(1024) void worklist_kernel(DecodeParams p, int unit
     p.ws.header[0] = 0u;
     p.ws.header[1] = acc;
     p.ws.header[2] = uint32_t(chunk);
-    p.ws.header[3] = nmerge;
   }
   __syncthreads();
-  // ... and the scatter
+  // pass 2: descriptors
   for (int b = tid; b < p.batch; b += 1024) {
     const SeqWork w = seq_work(p, b);
     const int n = n_items(w, chunk);
+    const int pbase = p.ws.item_base[b];
+    uint32_t fpos = uint32_t(p.ws.merge_list[b]);
     for (int k = 0; k < n; ++k) {
-      const uint32_t pos = atomicAdd(&bucket[kMaxChunkPages - item_cost(w, chunk, k)], 1u);
-      p.ws.items[pos] = make_int2(b, k);
+      const int pg = item_pages(w, chunk, k);
+      const uint32_t pos = pg == chunk ? fpos++ : atomicAdd(&bucket[kMaxChunkPages - pg], 1u);
+      write_item(p, pos, b, w, chunk, k, n, pbase);
     }
+    p.ws.item_count[b] = n;
   }
+  __syncthreads();
+  // list of split sequences for the merge (overwrites the scratch use above)
+  for (int b = tid; b < p.batch; b += 1024)
+    if (p.ws.item_count[b] > 1) p.ws.merge_list[atomicAdd(&nmerge, 1u)] = b;
+  __syncthreads();
+  if (tid == 0) p.ws.header[3] = nmerge;
 }
 
 // ------------------------------------------------------------- attention --
+struct ItemDesc {
+  int b, L, first, ck, npg, nitems, pbase, slot;
+};
+
+__device__ inline ItemDesc load_item(const DecodeParams& p, int64_t item) {
+  const int4 a = p.ws.items[2 * item];
+  const int4 c = p.ws.items[2 * item + 1];
+  ItemDesc d;
+  d.b = a.x;
+  d.L = a.y;
+  d.first = a.z;
+  d.ck = a.w >> 8;
+  d.npg = a.w & 0xFF;
+  d.nitems = c.x;
+  d.pbase = c.y;
+  d.slot = c.z;
+  return d;
+}
+
 template <int FMT, int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KV4_WAVES_PER_EU, 8))) void attention_kernel(
     DecodeParams p) {
@@ -568,24 +616,42 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KV4_WAVES_P
   const int ln = lane & 15, kg = lane >> 4;
   const int H = p.num_kv_heads, Hq = p.num_q_heads, G = Hq / H;
   const int NHB = (G + HB - 1) / HB;
+  const int UPI = H * NHB;  // units per item
   const int S = FMT == kFmtKV4 ? p.n_sink : 0;
   const int R = FMT == kFmtKV4 ? p.n_recent : 0;
-  const int64_t units = int64_t(p.ws.header[1]) * H * NHB;
-  const int chunk = int(p.ws.header[2]);
+  const int64_t units = int64_t(p.ws.header[1]) * UPI;
+  if (units == 0) return;
 
-  uint32_t nxt = 0;
-  if (lane == 0) nxt = atomicAdd(&p.ws.header[0], 1u);
-  int64_t uu = __builtin_amdgcn_readfirstlane(nxt);
-  while (uu < units) {
-    // fetch the next unit now; the atomic's latency hides behind this one
-    if (lane == 0) nxt = atomicAdd(&p.ws.header[0], 1u);
-    const int64_t item = uu / (H * NHB);
-    const int rem = int(uu % (H * NHB));
+  // Static round robin over the list (longest items first): in round k the
+  // waves hold units kN .. kN+N-1, so the kv heads of one item -- adjacent
+  // blocks of the same pages -- are read at the same time, which keeps DRAM
+  // rows open, and neighbouring waves have units of about the same size.  The
+  // next units are known in advance: the descriptor of unit k+2 and the page
+  // ids of unit k+1 are loaded when unit k starts.
+  const int64_t nw = int64_t(gridDim.x) * (blockDim.x / kWave);
+  auto item_of = [&](int64_t t) -> int64_t { return (t < units ? t : units - 1) / UPI; };
+  auto fetch_pids = [&](const ItemDesc& d) -> int {
+    int v = 0;
+    if (lane < d.npg) {
+      const int64_t x = p.page_table[int64_t(d.b) * p.max_pages + d.first + lane];
+      v = (x < 0 || x >= p.num_pages) ? -1 : int(x);
+    }
+    return v;
+  };
+  int64_t t0 = int64_t(blockIdx.x) * (blockDim.x / kWave) + threadIdx.x / kWave;
+  ItemDesc d0 = load_item(p, item_of(t0));
+  ItemDesc d1 = load_item(p, item_of(t0 + nw));
+  int pid0 = fetch_pids(d0);
+
+  for (; t0 < units; t0 += nw) {
+    // ---- run-ahead for the following units (fixed position, unconditional)
+    const ItemDesc d2 = load_item(p, item_of(t0 + 2 * nw));
+    const int pid1 = fetch_pids(d1);
+
+    const int rem = int(t0 % UPI);
     const int h = rem / NHB, hb = rem % NHB;
-    const int2 it = p.ws.items[item];
-    const int b = it.x, ck = it.y;
-    int L = p.seq_lens[b];
-    L = L < 0 ? 0 : (L > p.max_pages * kPage ? p.max_pages * kPage : L);
+    const ItemDesc d = d0;
+    const int b = d.b, L = d.L;
     const Regions g = regions(L, S, R);
 
     // ---- unit set-up: q operand of this lane's row (head hl, group grp)
@@ -631,54 +697,40 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KV4_WAVES_P
     }
 
     // ---- protected rows: INT8 side-cache tiles (sinks, then the ring)
-    if (FMT == kFmtKV4 && ck == 0 && L > 0 && S + R > 0) {
-      const int slot = p.slot_ids ? p.slot_ids[b] : b;
-      if (slot >= 0 && slot < p.num_slots) {
-        const int se = L < S ? L : S;
-        const int nring = L > S ? (L - S < R ? L - S : R) : 0;
-        const int rows = nring > 0 ? S + nring : se;
-        const int ntiles = (rows + kPage - 1) / kPage;
-        const uint8_t* sblk = p.side + (int64_t(slot) * H + h) * p.side_bytes;
-        auto ptr = [&](int i) { return sblk + int64_t(i) * int8_tile_bytes(D); };
-        auto mask = [&](int i) {
-          const int r0 = i * kPage;
-          return range_mask(0 - r0, se - r0) | range_mask(S - r0, S + nring - r0);
-        };
-        run_tiles<kInt8Tile, D, KV4_STAGES8>(u, ntiles, ptr, mask, lane);
-      }
+    if (FMT == kFmtKV4 && d.ck == 0 && L > 0 && S + R > 0 && d.slot >= 0 && d.slot < p.num_slots) {
+      const int se = L < S ? L : S;
+      const int nring = L > S ? (L - S < R ? L - S : R) : 0;
+      const int rows = nring > 0 ? S + nring : se;
+      const int ntiles = (rows + kPage - 1) / kPage;
+      const uint8_t* sblk = p.side + (int64_t(d.slot) * H + h) * p.side_bytes;
+      auto ptr = [&](int i) { return sblk + int64_t(i) * int8_tile_bytes(D); };
+      auto mask = [&](int i) {
+        const int r0 = i * kPage;
+        return range_mask(0 - r0, se - r0) | range_mask(S - r0, S + nring - r0);
+      };
+      run_tiles<kInt8Tile, D, KV4_STAGES8>(u, ntiles, ptr, mask, lane);
     }
 
-    // ---- middle pages of this item, page ids fetched 64 at a time
-    if (g.me > g.mb) {
-      const int first = g.mb / kPage + ck * chunk;
-      int last = first + chunk - 1;
-      if (last > (g.me - 1) / kPage) last = (g.me - 1) / kPage;
-      for (int base = first; base <= last; base += kWave) {
-        const int npg = (last - base + 1) < kWave ? (last - base + 1) : kWave;
-        int pid_l = 0;
-        if (lane < npg) {
-          const int64_t v = p.page_table[int64_t(b) * p.max_pages + base + lane];
-          pid_l = (v < 0 || v >= p.num_pages) ? -1 : int(v);
-        }
-        auto ptr = [&](int i) {
-          const int pid = __builtin_amdgcn_readlane(pid_l, i);
-          return p.pages + (int64_t(pid < 0 ? 0 : pid) * H + h) * p.block_bytes;
-        };
-        auto mask = [&](int i) {
-          const int pid = __builtin_amdgcn_readlane(pid_l, i);
-          const int p0 = (base + i) * kPage;
-          return pid < 0 ? 0u : range_mask(g.mb - p0, g.me - p0);
-        };
-        run_tiles<MAIN, D, MAIN == kInt4Page ? KV4_STAGES : (MAIN == kInt8Tile ? KV4_STAGES8 : 1)>(u, npg, ptr, mask, lane);
-      }
+    // ---- middle pages of this item (at most 64: one page id per lane)
+    if (d.npg > 0) {
+      auto ptr = [&](int i) {
+        const int pid = __builtin_amdgcn_readlane(pid0, i);
+        return p.pages + (int64_t(pid < 0 ? 0 : pid) * H + h) * p.block_bytes;
+      };
+      auto mask = [&](int i) {
+        const int pid = __builtin_amdgcn_readlane(pid0, i);
+        const int p0 = (d.first + i) * kPage;
+        return pid < 0 ? 0u : range_mask(g.mb - p0, g.me - p0);
+      };
+      run_tiles<MAIN, D, MAIN == kInt4Page ? KV4_STAGES : (MAIN == kInt8Tile ? KV4_STAGES8 : 1)>(u, d.npg, ptr,
+                                                                                                   mask, lane);
     }
 
     // ---- finish: per-head denominators, then output or partial
     float lt = u.l;
     lt += __shfl_xor(lt, 16, kWave);
     lt += __shfl_xor(lt, 32, kWave);
-    const int nitems = p.ws.item_count[b];
-    const int64_t pslot = int64_t(p.ws.item_base[b]) + ck;
+    const int64_t pslot = int64_t(d.pbase) + d.ck;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
 #pragma unroll
@@ -690,7 +742,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KV4_WAVES_P
         if (j < G) {
           const int hq = h * G + j;
           const int c = 16 * t + ln;
-          if (nitems == 1) {
+          if (d.nitems == 1) {
             const float v = lh > 0.f ? 16.0f * u.o[t][e] / lh : 0.f;
             p.out[(int64_t(b) * Hq + hq) * D + c] = f32_to_bf16_bits(v);
           } else {
@@ -703,7 +755,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KV4_WAVES_P
       const int j = hb * HB + ln / NG;
       if (j < G) {
         const int hq = h * G + j;
-        if (nitems == 1) {
+        if (d.nitems == 1) {
           if (p.lse) p.lse[int64_t(b) * Hq + hq] = lt > 0.f ? (u.m + log2f(lt)) * kLn2 : -INFINITY;
         } else {
           float* part = p.ws.partials + (pslot * Hq + hq) * (D + 2);
@@ -712,13 +764,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KV4_WAVES_P
         }
       }
     }
-    uu = __builtin_amdgcn_readfirstlane(nxt);
+    // ---- rotate the run-ahead state
+    d0 = d1;
+    d1 = d2;
+    pid0 = pid1;
   }
 }
 
 // ----------------------------------------------------------------- merge ---
 // Exact log-sum-exp merge of the partials of split sequences; a persistent
-// grid strides over (split sequence, query head) pairs.
+// grid strides over (split sequence, query head) pairs.  The lanes first read
+// the (m, l) of all items at once, then the output channels are combined.
 template <int D>
 __global__ __launch_bounds__(256) void merge_kernel(DecodeParams p) {
   constexpr int E = D / kWave;
@@ -730,22 +786,42 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeParams p) {
     const int b = p.ws.merge_list[w / Hq], hq = int(w % Hq);
     const int n = p.ws.item_count[b];
     const int64_t base = int64_t(p.ws.item_base[b]) * Hq + hq;
-    float M = -INFINITY;
-    for (int i = 0; i < n; ++i) {
-      const float* part = p.ws.partials + (base + int64_t(i) * Hq) * (D + 2);
-      if (part[D + 1] > 0.f) M = fmaxf(M, part[D]);
-    }
-    float l = 0.f, o[E];
+    float M = -INFINITY, l = 0.f, o[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) o[e] = 0.f;
-    for (int i = 0; i < n; ++i) {
-      const float* part = p.ws.partials + (base + int64_t(i) * Hq) * (D + 2);
-      const float li = part[D + 1];
-      if (!(li > 0.f)) continue;  // an item without context rows
-      const float a = __builtin_amdgcn_exp2f(part[D] - M);
-      l += a * li;
+    for (int i0 = 0; i0 < n; i0 += kWave) {
+      const int cnt = n - i0 < kWave ? n - i0 : kWave;
+      float mi = -INFINITY, li = 0.f;
+      if (lane < cnt) {
+        const float* part = p.ws.partials + (base + int64_t(i0 + lane) * Hq) * (D + 2);
+        mi = part[D];
+        li = part[D + 1];
+        if (!(li > 0.f)) mi = -INFINITY;  // an item without context rows
+      }
+      const float mc = wave_max<kWave>(mi);
+      const float Mn = fmaxf(M, mc);
+      if (Mn == -INFINITY) continue;
+      const float sc = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
+      const float wi = mi == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mi - Mn);
+      l = l * sc + wave_sum<kWave>(wi * li);
 #pragma unroll
-      for (int e = 0; e < E; ++e) o[e] = fmaf(a, part[lane * E + e], o[e]);
+      for (int e = 0; e < E; ++e) o[e] *= sc;
+      for (int i = 0; i < cnt; i += 4) {  // four independent loads in flight
+        float v[4][E], a[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          a[k] = __shfl(wi, i + k < cnt ? i + k : 0, kWave);
+          const float* part = p.ws.partials + (base + int64_t(i0 + (i + k < cnt ? i + k : i)) * Hq) * (D + 2);
+#pragma unroll
+          for (int e = 0; e < E; ++e) v[k][e] = part[lane * E + e];
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          if (i + k < cnt)
+#pragma unroll
+            for (int e = 0; e < E; ++e) o[e] = fmaf(a[k], v[k][e], o[e]);
+      }
+      M = Mn;
     }
     const float inv = l > 0.f ? 1.0f / l : 0.f;
 #pragma unroll
@@ -787,7 +863,7 @@ hipError_t launch_fd(DecodeParams p, hipStream_t stream) {
   hipLaunchKernelGGL((attention_kernel<FMT, D>), dim3(blocks), dim3(256), 0, stream, p);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL((merge_kernel<D>), dim3(cus * 2), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((merge_kernel<D>), dim3(cus * blocks_per_cu(merge_kernel<D>)), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -810,7 +886,7 @@ size_t decode_workspace_bytes(int32_t batch, int32_t max_pages, int32_t num_q_he
   const int64_t max_items = max_items_of(batch, max_pages);
   size_t s = 256;                                   // header
   s += 3 * align256(sizeof(int32_t) * size_t(batch));  // item_base, item_count, merge_list
-  s += align256(sizeof(int2) * size_t(max_items)); // items
+  s += align256(2 * sizeof(int4) * size_t(max_items)); // items
   s += align256(sizeof(float) * size_t(max_items) * num_q_heads * (head_dim + 2));
   return s;
 }
@@ -830,8 +906,8 @@ DecodeWorkspace carve_workspace(void* base, int32_t batch, int32_t max_pages, in
   q += align256(sizeof(int32_t) * size_t(batch));
   w.merge_list = reinterpret_cast<int32_t*>(q);
   q += align256(sizeof(int32_t) * size_t(batch));
-  w.items = reinterpret_cast<int2*>(q);
-  q += align256(sizeof(int2) * size_t(max_items));
+  w.items = reinterpret_cast<int4*>(q);
+  q += align256(2 * sizeof(int4) * size_t(max_items));
   w.partials = reinterpret_cast<float*>(q);
   w.max_items = max_items;
   return w;

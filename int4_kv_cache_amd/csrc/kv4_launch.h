@@ -37,7 +37,7 @@ struct DecodeWorkspace {
   int32_t* item_base;    // [batch] first partial slot of a split sequence
   int32_t* item_count;   // [batch]
   int32_t* merge_list;   // [batch] split sequences
-  int2* items;           // [max_items] (sequence, chunk index)
+  int4* items;           // [max_items][2] work-item descriptors (two int4 each)
   float* partials;       // [max_items][num_q_heads][head_dim + 2]
   int64_t max_items;
 };
