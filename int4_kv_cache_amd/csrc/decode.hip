@@ -80,6 +80,19 @@ __device__ inline uint32_t pack_exact(float lo, float hi) {
 }
 __device__ inline float h2f_lo(uint32_t w) { return f16_to_f32(uint16_t(w & 0xFFFF)); }
 __device__ inline float h2f_hi(uint32_t w) { return f16_to_f32(uint16_t(w >> 16)); }
+// x * (fp16 half of w) as one mixed-precision FMA.  The +0 addend keeps the
+// FMA from being folded into a multiply (and then into a neighbouring add);
+// the sign of a zero product is irrelevant to every use here.
+__device__ inline float mul_h_lo(float x, uint32_t w) { return fmaf(x, h2f_lo(w), 0.0f); }
+__device__ inline float mul_h_hi(float x, uint32_t w) { return fmaf(x, h2f_hi(w), 0.0f); }
+// max of three finite-or-infinite floats in one instruction (fmaxf would first
+// quiet signalling NaNs of operands the compiler cannot prove canonical; no
+// NaN reaches this point)
+__device__ inline float max3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
 __device__ inline float sbyte(uint32_t w, int k) { return float(int32_t(w << (24 - 8 * k)) >> 24); }
 
 // INT4: nibbles k and k+4 of d -> bf16 pair 1 + (code+8)/16.
@@ -106,6 +119,32 @@ __device__ inline float quad_xor2(float v) {
 }
 
 // ------------------------------------------------------------ tile loads --
+// Every load is (uniform block base) + (per-lane 32-bit offset, fixed for the
+// kernel), which maps to global_load with a scalar base and costs no vector
+// address arithmetic per tile.
+template <int KIND, int D>
+struct LaneOff {
+  uint32_t k, v, ks, vs;
+  __device__ inline LaneOff(int ln, int kg) {
+    constexpr int NG = D / 32;
+    if constexpr (KIND == kInt4Page) {
+      k = ln * (D / 2) + kg * (D / 8);
+      v = 8 * D + (kg * 16 + ln) * (D / 8);
+      ks = 16 * D + ((ln % NG) * 16 + kg * 4) * 2;
+      vs = ks + D;
+    } else if constexpr (KIND == kInt8Tile) {
+      k = ln * D + kg * (D / 4);
+      v = 16 * D + (kg * 16 + ln) * (D / 4);
+      ks = 32 * D + kg * 8;
+      vs = ks + 32;
+    } else {
+      k = (ln * D + kg * (D / 4)) * 2;
+      v = 32 * D + (kg * 16 + ln) * (D / 2);
+      ks = vs = 0;
+    }
+  }
+};
+
 template <int KIND, int D>
 struct Tile;
 
@@ -115,24 +154,20 @@ struct Tile<kInt4Page, D> {
   uint32_t k[KW];
   uint32_t v[KW];
   uint32_t ks[2], vs[2];  // fp16 scales of positions 4kg..4kg+3, group = ln % NG
-  __device__ inline void load(const uint8_t* __restrict__ blk, int ln, int kg) {
-    constexpr int NG = D / 32;
-    const int grp = ln % NG;
-    const uint8_t* kp = blk + ln * (D / 2) + kg * (D / 8);
-    const uint8_t* vp = blk + 8 * D + (kg * 16 + ln) * (D / 8);
+  __device__ inline void load(const uint8_t* __restrict__ blk, const LaneOff<kInt4Page, D>& o) {
     if constexpr (KW == 4) {
-      const uint4 a = *reinterpret_cast<const uint4*>(kp);
-      const uint4 b = *reinterpret_cast<const uint4*>(vp);
+      const uint4 a = *reinterpret_cast<const uint4*>(blk + o.k);
+      const uint4 b = *reinterpret_cast<const uint4*>(blk + o.v);
       k[0] = a.x; k[1] = a.y; k[2] = a.z; k[3] = a.w;
       v[0] = b.x; v[1] = b.y; v[2] = b.z; v[3] = b.w;
     } else {
-      const uint2 a = *reinterpret_cast<const uint2*>(kp);
-      const uint2 b = *reinterpret_cast<const uint2*>(vp);
+      const uint2 a = *reinterpret_cast<const uint2*>(blk + o.k);
+      const uint2 b = *reinterpret_cast<const uint2*>(blk + o.v);
       k[0] = a.x; k[1] = a.y;
       v[0] = b.x; v[1] = b.y;
     }
-    const uint2 s = *reinterpret_cast<const uint2*>(blk + 16 * D + (grp * 16 + kg * 4) * 2);
-    const uint2 t = *reinterpret_cast<const uint2*>(blk + 17 * D + (grp * 16 + kg * 4) * 2);
+    const uint2 s = *reinterpret_cast<const uint2*>(blk + o.ks);
+    const uint2 t = *reinterpret_cast<const uint2*>(blk + o.vs);
     ks[0] = s.x; ks[1] = s.y;
     vs[0] = t.x; vs[1] = t.y;
   }
@@ -144,18 +179,16 @@ struct Tile<kInt8Tile, D> {
   uint32_t k[KW];
   uint32_t v[KW];
   uint32_t ks[2], vs[2];
-  __device__ inline void load(const uint8_t* __restrict__ tile, int ln, int kg) {
-    const uint8_t* kp = tile + ln * D + kg * (D / 4);
-    const uint8_t* vp = tile + 16 * D + (kg * 16 + ln) * (D / 4);
+  __device__ inline void load(const uint8_t* __restrict__ tile, const LaneOff<kInt8Tile, D>& o) {
 #pragma unroll
     for (int i = 0; i < KW / 4; ++i) {
-      const uint4 a = reinterpret_cast<const uint4*>(kp)[i];
-      const uint4 b = reinterpret_cast<const uint4*>(vp)[i];
+      const uint4 a = *reinterpret_cast<const uint4*>(tile + o.k + 16 * i);
+      const uint4 b = *reinterpret_cast<const uint4*>(tile + o.v + 16 * i);
       k[4 * i] = a.x; k[4 * i + 1] = a.y; k[4 * i + 2] = a.z; k[4 * i + 3] = a.w;
       v[4 * i] = b.x; v[4 * i + 1] = b.y; v[4 * i + 2] = b.z; v[4 * i + 3] = b.w;
     }
-    const uint2 s = *reinterpret_cast<const uint2*>(tile + 32 * D + kg * 8);
-    const uint2 t = *reinterpret_cast<const uint2*>(tile + 32 * D + 32 + kg * 8);
+    const uint2 s = *reinterpret_cast<const uint2*>(tile + o.ks);
+    const uint2 t = *reinterpret_cast<const uint2*>(tile + o.vs);
     ks[0] = s.x; ks[1] = s.y;
     vs[0] = t.x; vs[1] = t.y;
   }
@@ -166,13 +199,11 @@ struct Tile<kBf16Page, D> {
   static constexpr int KW = D / 8;  // D/2 bytes per lane
   uint32_t k[KW];
   uint32_t v[KW];
-  __device__ inline void load(const uint8_t* __restrict__ tile, int ln, int kg) {
-    const uint8_t* kp = tile + (ln * D + kg * (D / 4)) * 2;
-    const uint8_t* vp = tile + 32 * D + (kg * 16 + ln) * (D / 2);
+  __device__ inline void load(const uint8_t* __restrict__ tile, const LaneOff<kBf16Page, D>& o) {
 #pragma unroll
     for (int i = 0; i < KW / 4; ++i) {
-      const uint4 a = reinterpret_cast<const uint4*>(kp)[i];
-      const uint4 b = reinterpret_cast<const uint4*>(vp)[i];
+      const uint4 a = *reinterpret_cast<const uint4*>(tile + o.k + 16 * i);
+      const uint4 b = *reinterpret_cast<const uint4*>(tile + o.v + 16 * i);
       k[4 * i] = a.x; k[4 * i + 1] = a.y; k[4 * i + 2] = a.z; k[4 * i + 3] = a.w;
       v[4 * i] = b.x; v[4 * i + 1] = b.y; v[4 * i + 2] = b.z; v[4 * i + 3] = b.w;
     }
@@ -187,6 +218,7 @@ struct Unit {
   bf16x8_t bq[NG];                   // q operand per QK MFMA
   float qsum;                        // sum of this lane's row (head, group) of q
   f32x4_t o[NT];                     // PV accumulators (D layout)
+  f32x4_t corr;                      // INT4 V-encoding correction per row (D layout)
   float m;                           // running max (log2 units) of head ln / NG
   float l;                           // this lane's share of the softmax denominator
   float qk_scale;                    // softmax_scale * log2(e)
@@ -225,10 +257,10 @@ __device__ inline void qk_tile(const Unit<D>& u, const Tile<KIND, D>& T, float (
 #pragma unroll
     for (int e = 0; e < 4; ++e) x[e] = acc[e];
   } else {
-    x[0] = acc[0] * h2f_lo(T.ks[0]);
-    x[1] = acc[1] * h2f_hi(T.ks[0]);
-    x[2] = acc[2] * h2f_lo(T.ks[1]);
-    x[3] = acc[3] * h2f_hi(T.ks[1]);
+    x[0] = mul_h_lo(acc[0], T.ks[0]);
+    x[1] = mul_h_hi(acc[1], T.ks[0]);
+    x[2] = mul_h_lo(acc[2], T.ks[1]);
+    x[3] = mul_h_hi(acc[3], T.ks[1]);
   }
 }
 
@@ -288,15 +320,14 @@ __device__ inline void step(Unit<D>& u, const Tile<KIND, D>& T0, const Tile<KIND
       x1[e] += quad_xor2(x1[e]);
     }
   }
-  float mx = -INFINITY;
+  if ((mask0 & mask1) != 0xFFFFu) {  // wave-uniform: only partial steps are masked
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    if constexpr (MASKED) {
+    for (int e = 0; e < 4; ++e) {
       x0[e] = ((va0 >> e) & 1u) ? x0[e] : -INFINITY;
       x1[e] = ((va1 >> e) & 1u) ? x1[e] : -INFINITY;
     }
-    mx = fmaxf(mx, fmaxf(x0[e], x1[e]));
   }
+  float mx = max3(max3(x0[0], x0[1], x0[2]), max3(x0[3], x1[0], x1[1]), max3(x1[2], x1[3], -INFINITY));
   // score (log2 units) = sc * x; INT4 partials carry the encoding's 1/16
   const float sc = KIND == kInt4Page ? 16.0f * u.qk_scale : u.qk_scale;
 
@@ -310,6 +341,8 @@ __device__ inline void step(Unit<D>& u, const Tile<KIND, D>& T0, const Tile<KIND
     const float alpha = (mn == u.m) ? 1.0f : __builtin_amdgcn_exp2f(u.m - mn);
     u.l *= alpha;
     u.m = mn;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) u.corr[e] *= head_value_for_acc<D>(alpha, lane, e);
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const int e0 = t / 2;
@@ -335,36 +368,41 @@ __device__ inline void step(Unit<D>& u, const Tile<KIND, D>& T0, const Tile<KIND
 #pragma unroll
     for (int e = 0; e < 8; ++e) ap[e] = pr[e] * 0.0625f;
   } else {
-    const float sv[8] = {h2f_lo(T0.vs[0]), h2f_hi(T0.vs[0]), h2f_lo(T0.vs[1]), h2f_hi(T0.vs[1]),
-                         h2f_lo(T1.vs[0]), h2f_hi(T1.vs[0]), h2f_lo(T1.vs[1]), h2f_hi(T1.vs[1])};
+    ap[0] = mul_h_lo(pr[0], T0.vs[0]);
+    ap[1] = mul_h_hi(pr[1], T0.vs[0]);
+    ap[2] = mul_h_lo(pr[2], T0.vs[1]);
+    ap[3] = mul_h_hi(pr[3], T0.vs[1]);
+    ap[4] = mul_h_lo(pr[4], T1.vs[0]);
+    ap[5] = mul_h_hi(pr[5], T1.vs[0]);
+    ap[6] = mul_h_lo(pr[6], T1.vs[1]);
+    ap[7] = mul_h_hi(pr[7], T1.vs[1]);
+    if constexpr (KIND != kInt4Page) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) ap[e] = KIND == kInt4Page ? pr[e] * sv[e] : pr[e] * (sv[e] * 0.0625f);
+      for (int e = 0; e < 8; ++e) ap[e] *= 0.0625f;
+    }
   }
   uint32_t hi[4], lo[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     hi[j] = pack_bf16(ap[2 * j], ap[2 * j + 1]);
-    lo[j] = pack_bf16(ap[2 * j] - bf16_lo(hi[j]), ap[2 * j + 1] - bf16_hi(hi[j]));
+    // low half moved up with a byte permute (0x0c selects a zero byte)
+    const float h0 = __uint_as_float(__builtin_amdgcn_perm(0u, hi[j], 0x01000c0cu));
+    lo[j] = pack_bf16(ap[2 * j] - h0, ap[2 * j + 1] - bf16_hi(hi[j]));
   }
   const bf16x8_t a_hi = bf8(hi[0], hi[1], hi[2], hi[3]);
   const bf16x8_t a_lo = bf8(lo[0], lo[1], lo[2], lo[3]);
 
-  f32x4_t corr = {0.f, 0.f, 0.f, 0.f};
   if constexpr (KIND == kInt4Page) {
-    // -1.5 * sum over the 32 positions of this row's A: removes the constant
-    // part of the 1 + (code+8)/16 encoding of the V codes.
+    // -1.5 * sum over the positions of this row's A: the constant part of the
+    // 1 + (code+8)/16 encoding of the V codes, added to the output at the end.
     const bf16x8_t ones = bf8(0xBFC0BFC0u, 0xBFC0BFC0u, 0xBFC0BFC0u, 0xBFC0BFC0u);
-    corr = mfma(a_hi, ones, corr);
-    corr = mfma(a_lo, ones, corr);
+    u.corr = mfma(a_hi, ones, u.corr);
+    u.corr = mfma(a_lo, ones, u.corr);
   }
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     const bf16x8_t bv = v_operand<KIND, D>(T0, T1, t);
     f32x4_t c = u.o[t];
-    if constexpr (KIND == kInt4Page) {
-      c[t / 2] += corr[t / 2];
-      if constexpr (NG == 2) c[t / 2 + 2] += corr[t / 2 + 2];
-    }
     c = mfma(a_hi, bv, c);
     c = mfma(a_lo, bv, c);
     u.o[t] = c;
@@ -380,14 +418,14 @@ __device__ inline void step(Unit<D>& u, const Tile<KIND, D>& T0, const Tile<KIND
 template <int KIND, int D, int STAGES, class PtrFn, class MaskFn>
 __device__ inline void run_tiles(Unit<D>& u, int n, PtrFn ptr, MaskFn mask, int lane) {
   if (n <= 0) return;
-  const int ln = lane & 15, kg = lane >> 4;
+  const LaneOff<KIND, D> off(lane & 15, lane >> 4);
   const int nsteps = (n + 1) >> 1;
   const int last = nsteps - 1;
   auto load = [&](Tile<KIND, D>& t0, Tile<KIND, D>& t1, int s) {
     s = s < last ? s : last;
     const int i = 2 * s;
-    t0.load(ptr(i), ln, kg);
-    t1.load(ptr(i + 1 < n ? i + 1 : i), ln, kg);
+    t0.load(ptr(i), off);
+    t1.load(ptr(i + 1 < n ? i + 1 : i), off);
   };
   auto run = [&](const Tile<KIND, D>& t0, const Tile<KIND, D>& t1, int s) {
     const int i = 2 * s;
@@ -592,18 +630,32 @@ struct ItemDesc {
   int b, L, first, ck, npg, nitems, pbase, slot;
 };
 
-__device__ inline ItemDesc load_item(const DecodeParams& p, int64_t item) {
-  const int4 a = p.ws.items[2 * item];
-  const int4 c = p.ws.items[2 * item + 1];
+// A work-item descriptor as loaded (two int4, identical in every lane) and its
+// decoded form.  Decoding makes the fields explicitly wave-uniform so that the
+// loop control and the page addresses derived from them live in scalar
+// registers; it waits for the load, so it is done one unit after the load was
+// issued.
+struct RawItem {
+  int4 a, c;
+};
+
+__device__ inline int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+__device__ inline RawItem load_item(const DecodeParams& p, int64_t item) {
+  return RawItem{p.ws.items[2 * item], p.ws.items[2 * item + 1]};
+}
+
+__device__ inline ItemDesc decode_item(const RawItem& r) {
   ItemDesc d;
-  d.b = a.x;
-  d.L = a.y;
-  d.first = a.z;
-  d.ck = a.w >> 8;
-  d.npg = a.w & 0xFF;
-  d.nitems = c.x;
-  d.pbase = c.y;
-  d.slot = c.z;
+  d.b = uniform(r.a.x);
+  d.L = uniform(r.a.y);
+  d.first = uniform(r.a.z);
+  const int w = uniform(r.a.w);
+  d.ck = w >> 8;
+  d.npg = w & 0xFF;
+  d.nitems = uniform(r.c.x);
+  d.pbase = uniform(r.c.y);
+  d.slot = uniform(r.c.z);
   return d;
 }
 
@@ -638,14 +690,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KV4_WAVES_P
     }
     return v;
   };
-  int64_t t0 = int64_t(blockIdx.x) * (blockDim.x / kWave) + threadIdx.x / kWave;
-  ItemDesc d0 = load_item(p, item_of(t0));
-  ItemDesc d1 = load_item(p, item_of(t0 + nw));
+  int64_t t0 = int64_t(blockIdx.x) * (blockDim.x / kWave) + uniform(threadIdx.x / kWave);
+  ItemDesc d0 = decode_item(load_item(p, item_of(t0)));
+  RawItem r1 = load_item(p, item_of(t0 + nw));
   int pid0 = fetch_pids(d0);
 
   for (; t0 < units; t0 += nw) {
     // ---- run-ahead for the following units (fixed position, unconditional)
-    const ItemDesc d2 = load_item(p, item_of(t0 + 2 * nw));
+    const RawItem r2 = load_item(p, item_of(t0 + 2 * nw));
+    const ItemDesc d1 = decode_item(r1);
     const int pid1 = fetch_pids(d1);
 
     const int rem = int(t0 % UPI);
@@ -691,6 +744,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KV4_WAVES_P
       u.qsum = float(qs);
 #pragma unroll
       for (int t = 0; t < NT; ++t) u.o[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      u.corr = f32x4_t{0.f, 0.f, 0.f, 0.f};
       u.m = -INFINITY;
       u.l = 0.f;
       u.qk_scale = p.softmax_scale * kLog2e;
@@ -742,11 +796,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KV4_WAVES_P
         if (j < G) {
           const int hq = h * G + j;
           const int c = 16 * t + ln;
+          const float o = u.o[t][e] + u.corr[e];
           if (d.nitems == 1) {
-            const float v = lh > 0.f ? 16.0f * u.o[t][e] / lh : 0.f;
+            const float v = lh > 0.f ? 16.0f * o / lh : 0.f;
             p.out[(int64_t(b) * Hq + hq) * D + c] = f32_to_bf16_bits(v);
           } else {
-            p.ws.partials[(pslot * Hq + hq) * (D + 2) + c] = 16.0f * u.o[t][e];
+            p.ws.partials[(pslot * Hq + hq) * (D + 2) + c] = 16.0f * o;
           }
         }
       }
@@ -766,7 +821,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KV4_WAVES_P
     }
     // ---- rotate the run-ahead state
     d0 = d1;
-    d1 = d2;
+    r1 = r2;
     pid0 = pid1;
   }
 }
