@@ -8,11 +8,13 @@ token per sequence, then kv4_decode_attention.  Inputs are synthetic, seeded
 and already resident in HBM when timing starts.
 
 Prints one JSON line.  `value` is context tokens per second (sum of the
-sequences' context lengths / step time).  `roofline` is for the decode call
-(work-list + attention + merge kernels, timed with HIP events on the stream
-they run on) against the 8 TB/s HBM peak, with the algorithmic bytes of the
-decode.  `cpu_baseline` times the CPU oracle on a bounded sample of the same
-workload.
+sequences' context lengths / step time).  The decode runs as its three phases
+(kv4_decode_phases: plan, attend, merge), each bracketed by HIP events on the
+stream it runs on.  `roofline` is for the dominant kernel, the attention
+kernel of the ATTEND phase, against the 8 TB/s HBM peak with its algorithmic
+bytes; `traffic` is the HBM bytes per launch from the committed rocprofv3
+counter runs (null once the kernel sources differ from the ones measured).
+`cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--variants] [--no-cpu]
 """
@@ -69,34 +71,89 @@ def algorithmic_bytes(wl, fmt):
     return int(kv + other)
 
 
+def attend_bytes(wl, fmt):
+    """Algorithmic bytes credited to the ATTEND phase (the attention kernel):
+    the decode's bytes less the bf16 output and the lse, which the merge
+    writes for sequences split over several work items (0.3% of the total at
+    the Qwen3-8B batch; leaving all of it out under-counts slightly)."""
+    cfg = wl.cfg
+    B = wl.lengths.size
+    return int(algorithmic_bytes(wl, fmt) - B * cfg.num_q_heads * (cfg.head_dim * 2 + 4))
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_kv4_qwen3-8b-b1024_traffic.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "int4_kv_cache_amd", "csrc", f)
+                  for f in ("decode.hip", "kv4_common.h", "kv4_launch.h")]
+
+
+def kernel_source_hash():
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per ATTEND launch from the committed rocprofv3 counter runs,
+    or None when the kernel sources changed since they were taken."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
 def time_steps(wl, steps, warmup, append=True):
+    """Time `steps` decode steps after `warmup` untimed ones.
+
+    A step is kv4_append of one token per sequence (if `append`), then the
+    decode as its three phases (plan, attend, merge) on the same stream, each
+    bracketed by HIP events on that stream.  Returns the mean ms per step over
+    the whole timed region and per-step ms arrays of every phase.
+    """
     import torch
 
+    import int4_kv_cache_amd as kv4
+
     stream = torch.cuda.current_stream()
+
+    def phase(mask):
+        kv4.decode_phases(wl.cache, wl.batch, wl.q, wl.out, wl.lse, wl.workspace, mask)
+
     for _ in range(warmup):
         if append:
             wl.step_append()
         wl.decode()
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-           torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0.record(stream)
-    for a, b, c in ev:
-        a.record(stream)
+    for e in ev:
+        e[0].record(stream)
         if append:
             wl.step_append()
-        b.record(stream)
-        wl.decode()
-        c.record(stream)
+        e[1].record(stream)
+        phase(kv4.PHASE_PLAN)
+        e[2].record(stream)
+        phase(kv4.PHASE_ATTEND)
+        e[3].record(stream)
+        phase(kv4.PHASE_MERGE)
+        e[4].record(stream)
     t1.record(stream)
     torch.cuda.synchronize()
     total_ms = t0.elapsed_time(t1)
-    app = np.array([a.elapsed_time(b) for a, b, _ in ev])
-    dec = np.array([b.elapsed_time(c) for _, b, c in ev])
-    return total_ms / steps, app, dec
+    ph = {name: np.array([e[i].elapsed_time(e[i + 1]) for e in ev])
+          for i, name in enumerate(("append", "plan", "attend", "merge"))}
+    ph["decode"] = ph["plan"] + ph["attend"] + ph["merge"]
+    return total_ms / steps, ph
 
 
 def cpu_baseline(wl, budget_s=12.0, max_seqs=256):
@@ -118,8 +175,9 @@ def cpu_baseline(wl, budget_s=12.0, max_seqs=256):
         ocache, pt, lens = pu.oracle_cache_for(wl, sample)
         q = np.ascontiguousarray(wl.host_q()[sample])
         # the step: append the last token of each sampled sequence, then decode
-        k_last = np.stack([wl.host_tokens(int(b))[0][-1] for b in sample])
-        v_last = np.stack([wl.host_tokens(int(b))[1][-1] for b in sample])
+        last = [wl.host_tokens(int(b)) for b in sample]
+        k_last = np.stack([k[-1] for k, _ in last])
+        v_last = np.stack([v[-1] for _, v in last])
         cu = np.arange(len(sample) + 1, dtype=np.int32)
         t = time.perf_counter()
         oracle.append(ocache, pt, lens, None, k_last, v_last, cu)
@@ -140,8 +198,8 @@ def cpu_baseline(wl, budget_s=12.0, max_seqs=256):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--variants", action="store_true", help="also time kv8 / bf16 / plain INT4")
     ap.add_argument("--no-cpu", action="store_true")
     args = ap.parse_args()
@@ -160,10 +218,11 @@ def main():
     wl = build_config(CFG_IDX, kv4.FMT_KV4, keep_inputs=not args.no_cpu)
     ctx = int(wl.lengths.sum())
     print(f"[bench] built: batch {wl.lengths.size}, ctx tokens {ctx}", file=sys.stderr, flush=True)
-    ms, app, dec = time_steps(wl, args.steps, args.warmup)
+    ms, ph = time_steps(wl, args.steps, args.warmup)
     abytes = algorithmic_bytes(wl, 0)
-    dec_ms = float(np.mean(dec))
-    achieved = abytes / (dec_ms * 1e-3) / 1e9
+    att_ms = float(np.mean(ph["attend"]))
+    achieved = attend_bytes(wl, 0) / (att_ms * 1e-3) / 1e9
+    us = {k: float(np.mean(v)) * 1e3 for k, v in ph.items()}
     result = {
         "metric": "KV4 decode-attention ctx tokens/s (us/step and % HBM peak alongside), Qwen3-8B shape",
         "value": ctx / (ms * 1e-3),
@@ -175,28 +234,35 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int4/int8 codes, fp32 accumulate, bf16 out",
+        "dtype": "int4/int8 codes x bf16 q on bf16 MFMA, fp32 accumulate, bf16 out",
         "data": "synthetic (seeded)",
         "config": {"workload": "qwen3-8b-layer-b1024: 1024 seqs (128 groups x 8, shared 256-token "
                                "prompt), lognormal responses mean 2k cap 16384, Hq 32 / Hkv 8 / D 128, "
-                               "16 sinks + 128 recent INT8",
+                               "16 sinks + 128 recent INT8; step = append 1 token/seq + decode",
                    "global_batch": int(wl.lengths.size), "ctx_tokens": ctx,
-                   "append_us": float(np.mean(app)) * 1e3, "decode_us": dec_ms * 1e3,
-                   "decode_us_median": float(np.median(dec)) * 1e3},
+                   "append_us": us["append"], "plan_us": us["plan"], "attend_us": us["attend"],
+                   "merge_us": us["merge"], "decode_us": us["decode"],
+                   "decode_us_median": float(np.median(ph["decode"])) * 1e3,
+                   "decode_hbm_frac": abytes / (us["decode"] * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                   "decode_algorithmic_bytes": abytes},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "kv4_decode_attention (worklist + attention + merge)",
-                     "algorithmic_bytes": abytes},
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(),
+                     "kernel": "attention_kernel<kv4, 128> (the ATTEND phase)",
+                     "algorithmic_bytes": attend_bytes(wl, 0)},
     }
     if args.variants:
         var = {}
         for fmt, name, S, R in ((kv4.FMT_KV8, "kv8", 0, 0), (kv4.FMT_BF16, "bf16", 0, 0),
                                 (kv4.FMT_KV4, "int4_plain", 0, 0)):
             w2 = build_config(CFG_IDX, fmt, n_sink=S, n_recent=R)
-            _, _, d2 = time_steps(w2, max(5, args.steps // 2), 3, append=False)
+            w2.step_append()
+            _, p2 = time_steps(w2, max(10, args.steps // 2), 3, append=False)
             b2 = algorithmic_bytes(w2, fmt)
-            var[name] = {"decode_us": float(np.mean(d2)) * 1e3,
-                         "hbm_frac": b2 / (float(np.mean(d2)) * 1e-3) / 1e9 / HBM_PEAK_GBS}
+            d2 = float(np.mean(p2["decode"]))
+            a2 = float(np.mean(p2["attend"]))
+            var[name] = {"decode_us": d2 * 1e3, "attend_us": a2 * 1e3,
+                         "decode_hbm_frac": b2 / (d2 * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                         "attend_hbm_frac": attend_bytes(w2, fmt) / (a2 * 1e-3) / 1e9 / HBM_PEAK_GBS}
             del w2
             torch.cuda.empty_cache()
         result["variants"] = var

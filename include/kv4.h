@@ -176,7 +176,8 @@ kv4_status kv4_decode_workspace_size(const kv4_layout* layout, int32_t batch,
  *   lse    fp32 [batch][num_q_heads] natural-log sum of exp, or NULL
  * softmax_scale must be positive and finite (KV4_ERR_INVALID_ARG otherwise).
  * L = 0 gives out = 0 and lse = -inf.  Arithmetic: exact dequantized
- * products, fp32 accumulation.  The workspace is scratch for this call. */
+ * products, fp32 accumulation.  The workspace is scratch for this call
+ * (PLAN + ATTEND + MERGE of kv4_decode_phases). */
 kv4_status kv4_decode_attention(const kv4_layout* layout, const kv4_cache* cache,
                                 const kv4_batch* batch, const uint16_t* q,
                                 float softmax_scale, uint16_t* out, float* lse,
@@ -195,6 +196,44 @@ kv4_status kvbf16_decode_attention(const kv4_layout* layout, const kv4_cache* ca
                                    float softmax_scale, uint16_t* out, float* lse,
                                    void* workspace, size_t workspace_bytes,
                                    hipStream_t stream);
+
+/* ---- decode in phases -------------------------------------------------------
+ * A decode call is three kernels in stream order; *_decode_attention runs all
+ * three.  The phased form runs the ones selected by `phases` (bit mask):
+ *   KV4_PHASE_PLAN    work list of the batch (reads seq_lens; writes the
+ *                     workspace's plan).  The plan depends only on the format,
+ *                     the layout, batch, max_pages, seq_lens and slot_ids.
+ *   KV4_PHASE_ATTEND  attention over the planned work items: sequences held
+ *                     by one item get out / lse, split ones leave fp32
+ *                     partials in the workspace.
+ *   KV4_PHASE_MERGE   exact log-sum-exp merge of those partials into out / lse
+ *                     ([NEWS] Interpretation para 3).
+ * The caller orders the phases on streams.  After one PLAN, any number of
+ * ATTEND+MERGE pairs may use the plan while the inputs it depends on are
+ * unchanged -- e.g. every layer of a decode step, whose layers share the page
+ * table and seq_lens but have their own cache and q.  A plan is only valid
+ * for the function (format) that made it.  ATTEND+MERGE pairs that share a
+ * workspace must not overlap (the partials live there).  Arguments and
+ * errors as for *_decode_attention; `phases` outside 1..7 is
+ * KV4_ERR_INVALID_ARG; q/out/cache are not read by PLAN alone (may be NULL). */
+#define KV4_PHASE_PLAN 1u
+#define KV4_PHASE_ATTEND 2u
+#define KV4_PHASE_MERGE 4u
+kv4_status kv4_decode_phases(const kv4_layout* layout, const kv4_cache* cache,
+                             const kv4_batch* batch, const uint16_t* q,
+                             float softmax_scale, uint16_t* out, float* lse,
+                             void* workspace, size_t workspace_bytes,
+                             uint32_t phases, hipStream_t stream);
+kv4_status kv8_decode_phases(const kv4_layout* layout, const kv4_cache* cache,
+                             const kv4_batch* batch, const uint16_t* q,
+                             float softmax_scale, uint16_t* out, float* lse,
+                             void* workspace, size_t workspace_bytes,
+                             uint32_t phases, hipStream_t stream);
+kv4_status kvbf16_decode_phases(const kv4_layout* layout, const kv4_cache* cache,
+                                const kv4_batch* batch, const uint16_t* q,
+                                float softmax_scale, uint16_t* out, float* lse,
+                                void* workspace, size_t workspace_bytes,
+                                uint32_t phases, hipStream_t stream);
 
 /* ---- measurement aid ----------------------------------------------------------
  * Streams `bytes` (a multiple of 16) of `buf` through 128-bit loads and

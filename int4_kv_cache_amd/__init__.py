@@ -54,6 +54,7 @@ EXPORTS = [
     "kv4_append", "kv8_append", "kvbf16_append",
     "kv4_decode_workspace_size",
     "kv4_decode_attention", "kv8_decode_attention", "kvbf16_decode_attention",
+    "kv4_decode_phases", "kv8_decode_phases", "kvbf16_decode_phases",
     "kv4_probe_blocks", "kv4_hbm_read_probe",
 ]
 
@@ -84,6 +85,9 @@ def load(path: Optional[str] = None):
         f = getattr(L, f"{pre}_decode_attention")
         f.restype = ctypes.c_int
         f.argtypes = [P, P, P, P, ctypes.c_float, P, P, P, sz, P]
+        f = getattr(L, f"{pre}_decode_phases")
+        f.restype = ctypes.c_int
+        f.argtypes = [P, P, P, P, ctypes.c_float, P, P, P, sz, ctypes.c_uint32, P]
     L.kv4_decode_workspace_size.restype = ctypes.c_int
     L.kv4_decode_workspace_size.argtypes = [P, i32, i32, ctypes.POINTER(sz)]
     L.kv4_probe_blocks.restype = i32
@@ -189,6 +193,21 @@ def decode(cache: Cache, batch: Batch, q, out, lse, workspace, softmax_scale: fl
     st = getattr(load(), fn)(ctypes.byref(lay), ctypes.byref(cd), ctypes.byref(bd), _ptr(q),
                              float(softmax_scale), _ptr(out), _ptr(lse), _ptr(workspace),
                              int(workspace.numel()), _stream(stream))
+    _check(fn, st)
+
+
+PHASE_PLAN, PHASE_ATTEND, PHASE_MERGE = 1, 2, 4
+
+
+def decode_phases(cache: Cache, batch: Batch, q, out, lse, workspace, phases: int,
+                  softmax_scale: float = 1.0, stream=None):
+    """The selected phases of a decode (PHASE_PLAN | PHASE_ATTEND | PHASE_MERGE);
+    a plan in `workspace` serves later ATTEND/MERGE calls over the same batch."""
+    fn = f"{_PREFIX[cache.fmt]}_decode_phases"
+    lay, cd, bd = cache.layout, cache.desc(), batch.desc()
+    st = getattr(load(), fn)(ctypes.byref(lay), ctypes.byref(cd), ctypes.byref(bd), _ptr(q),
+                             float(softmax_scale), _ptr(out), _ptr(lse), _ptr(workspace),
+                             int(workspace.numel()), int(phases), _stream(stream))
     _check(fn, st)
 
 

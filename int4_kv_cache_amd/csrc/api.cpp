@@ -91,21 +91,33 @@ kv4_status append_impl(int fmt, const kv4_layout* L, const kv4_cache* c, const k
 
 kv4_status decode_impl(int fmt, const kv4_layout* L, const kv4_cache* c, const kv4_batch* b,
                        const uint16_t* q, float sm, uint16_t* out, float* lse, void* ws, size_t ws_bytes,
-                       hipStream_t stream) {
+                       unsigned phases, hipStream_t stream) {
+  if (phases < 1u || phases > 7u) return KV4_ERR_INVALID_ARG;
   kv4_status s = layout_check(L, fmt);
   if (s != KV4_OK) return s;
-  s = cache_batch_check(L, c, b, fmt);
-  if (s != KV4_OK) return s;
+  if (!b) return KV4_ERR_INVALID_ARG;
+  const bool plan_only = phases == KV4_PHASE_PLAN;
+  if (plan_only) {
+    if (b->batch < 0 || b->max_pages <= 0) return KV4_ERR_INVALID_ARG;
+    if (b->batch > 0 && (!b->page_table || !b->seq_lens)) return KV4_ERR_INVALID_ARG;
+  } else {
+    s = cache_batch_check(L, c, b, fmt);
+    if (s != KV4_OK) return s;
+  }
   if (b->batch == 0) return KV4_OK;
-  if (!q || !out || !ws) return KV4_ERR_INVALID_ARG;
+  if (!ws) return KV4_ERR_INVALID_ARG;
+  if ((phases & (KV4_PHASE_ATTEND | KV4_PHASE_MERGE)) && !out) return KV4_ERR_INVALID_ARG;
+  if ((phases & KV4_PHASE_ATTEND) && !q) return KV4_ERR_INVALID_ARG;
   if (!(sm > 0.0f) || sm > 3.0e38f) return KV4_ERR_INVALID_ARG;  // positive and finite
   const size_t need = kv4::decode_workspace_bytes(b->batch, b->max_pages, L->num_q_heads, L->head_dim);
   if (ws_bytes < need) return KV4_ERR_WORKSPACE;
   kv4::DecodeParams p{};
-  p.pages = static_cast<const uint8_t*>(c->pages);
-  p.num_pages = c->num_pages;
-  p.side = static_cast<const uint8_t*>(c->side);
-  p.num_slots = c->num_slots;
+  if (c) {
+    p.pages = static_cast<const uint8_t*>(c->pages);
+    p.num_pages = c->num_pages;
+    p.side = static_cast<const uint8_t*>(c->side);
+    p.num_slots = c->num_slots;
+  }
   p.page_table = b->page_table;
   p.max_pages = b->max_pages;
   p.seq_lens = b->seq_lens;
@@ -126,8 +138,10 @@ kv4_status decode_impl(int fmt, const kv4_layout* L, const kv4_cache* c, const k
     p.side = nullptr;
     p.num_slots = 0;
   }
-  return kv4::launch_decode(fmt, p, L->head_dim, stream) == hipSuccess ? KV4_OK : KV4_ERR_LAUNCH;
+  return kv4::launch_decode(fmt, p, L->head_dim, phases, stream) == hipSuccess ? KV4_OK : KV4_ERR_LAUNCH;
 }
+
+constexpr unsigned kAllPhases = KV4_PHASE_PLAN | KV4_PHASE_ATTEND | KV4_PHASE_MERGE;
 
 }  // namespace
 
@@ -174,17 +188,33 @@ kv4_status kv4_decode_workspace_size(const kv4_layout* L, int32_t batch, int32_t
 kv4_status kv4_decode_attention(const kv4_layout* L, const kv4_cache* c, const kv4_batch* b, const uint16_t* q,
                                 float sm, uint16_t* out, float* lse, void* ws, size_t ws_bytes,
                                 hipStream_t stream) {
-  return decode_impl(kFmtKV4, L, c, b, q, sm, out, lse, ws, ws_bytes, stream);
+  return decode_impl(kFmtKV4, L, c, b, q, sm, out, lse, ws, ws_bytes, kAllPhases, stream);
 }
 kv4_status kv8_decode_attention(const kv4_layout* L, const kv4_cache* c, const kv4_batch* b, const uint16_t* q,
                                 float sm, uint16_t* out, float* lse, void* ws, size_t ws_bytes,
                                 hipStream_t stream) {
-  return decode_impl(kFmtKV8, L, c, b, q, sm, out, lse, ws, ws_bytes, stream);
+  return decode_impl(kFmtKV8, L, c, b, q, sm, out, lse, ws, ws_bytes, kAllPhases, stream);
 }
 kv4_status kvbf16_decode_attention(const kv4_layout* L, const kv4_cache* c, const kv4_batch* b,
                                    const uint16_t* q, float sm, uint16_t* out, float* lse, void* ws,
                                    size_t ws_bytes, hipStream_t stream) {
-  return decode_impl(kFmtBF16, L, c, b, q, sm, out, lse, ws, ws_bytes, stream);
+  return decode_impl(kFmtBF16, L, c, b, q, sm, out, lse, ws, ws_bytes, kAllPhases, stream);
+}
+
+kv4_status kv4_decode_phases(const kv4_layout* L, const kv4_cache* c, const kv4_batch* b, const uint16_t* q,
+                             float sm, uint16_t* out, float* lse, void* ws, size_t ws_bytes, uint32_t phases,
+                             hipStream_t stream) {
+  return decode_impl(kFmtKV4, L, c, b, q, sm, out, lse, ws, ws_bytes, phases, stream);
+}
+kv4_status kv8_decode_phases(const kv4_layout* L, const kv4_cache* c, const kv4_batch* b, const uint16_t* q,
+                             float sm, uint16_t* out, float* lse, void* ws, size_t ws_bytes, uint32_t phases,
+                             hipStream_t stream) {
+  return decode_impl(kFmtKV8, L, c, b, q, sm, out, lse, ws, ws_bytes, phases, stream);
+}
+kv4_status kvbf16_decode_phases(const kv4_layout* L, const kv4_cache* c, const kv4_batch* b, const uint16_t* q,
+                                float sm, uint16_t* out, float* lse, void* ws, size_t ws_bytes, uint32_t phases,
+                                hipStream_t stream) {
+  return decode_impl(kFmtBF16, L, c, b, q, sm, out, lse, ws, ws_bytes, phases, stream);
 }
 
 int32_t kv4_probe_blocks(void) { return kv4::probe_blocks(); }

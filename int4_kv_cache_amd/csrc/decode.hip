@@ -904,27 +904,36 @@ int device_cus() {
 }
 
 template <int FMT, int D>
-hipError_t launch_fd(DecodeParams p, hipStream_t stream) {
+hipError_t launch_fd(DecodeParams p, unsigned phases, hipStream_t stream) {
   constexpr int HB = 16 / (D / 32);
   const int cus = device_cus();
   if (cus <= 0) return hipErrorInvalidDevice;
+  // the work list is sized for the attention grid, so both use the same count
   const int blocks = cus * blocks_per_cu(attention_kernel<FMT, D>);
   p.resident_waves = blocks * 4;
-  const int G = p.num_q_heads / p.num_kv_heads;
-  const int units_per_item = p.num_kv_heads * ((G + HB - 1) / HB);
-  hipLaunchKernelGGL(worklist_kernel, dim3(1), dim3(1024), 0, stream, p, units_per_item);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  hipLaunchKernelGGL((attention_kernel<FMT, D>), dim3(blocks), dim3(256), 0, stream, p);
-  err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  hipLaunchKernelGGL((merge_kernel<D>), dim3(cus * blocks_per_cu(merge_kernel<D>)), dim3(256), 0, stream, p);
-  return hipGetLastError();
+  if (phases & 1u) {
+    const int G = p.num_q_heads / p.num_kv_heads;
+    const int units_per_item = p.num_kv_heads * ((G + HB - 1) / HB);
+    hipLaunchKernelGGL(worklist_kernel, dim3(1), dim3(1024), 0, stream, p, units_per_item);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  if (phases & 2u) {
+    hipLaunchKernelGGL((attention_kernel<FMT, D>), dim3(blocks), dim3(256), 0, stream, p);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  if (phases & 4u) {
+    hipLaunchKernelGGL((merge_kernel<D>), dim3(cus * blocks_per_cu(merge_kernel<D>)), dim3(256), 0, stream, p);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  return hipSuccess;
 }
 
 template <int FMT>
-hipError_t launch_fmt(const DecodeParams& p, int head_dim, hipStream_t stream) {
-  return head_dim == 128 ? launch_fd<FMT, 128>(p, stream) : launch_fd<FMT, 64>(p, stream);
+hipError_t launch_fmt(const DecodeParams& p, int head_dim, unsigned phases, hipStream_t stream) {
+  return head_dim == 128 ? launch_fd<FMT, 128>(p, phases, stream) : launch_fd<FMT, 64>(p, phases, stream);
 }
 
 }  // namespace
@@ -968,10 +977,10 @@ DecodeWorkspace carve_workspace(void* base, int32_t batch, int32_t max_pages, in
   return w;
 }
 
-hipError_t launch_decode(int fmt, const DecodeParams& p, int head_dim, hipStream_t stream) {
-  if (fmt == kFmtKV4) return launch_fmt<kFmtKV4>(p, head_dim, stream);
-  if (fmt == kFmtKV8) return launch_fmt<kFmtKV8>(p, head_dim, stream);
-  return launch_fmt<kFmtBF16>(p, head_dim, stream);
+hipError_t launch_decode(int fmt, const DecodeParams& p, int head_dim, unsigned phases, hipStream_t stream) {
+  if (fmt == kFmtKV4) return launch_fmt<kFmtKV4>(p, head_dim, phases, stream);
+  if (fmt == kFmtKV8) return launch_fmt<kFmtKV8>(p, head_dim, phases, stream);
+  return launch_fmt<kFmtBF16>(p, head_dim, phases, stream);
 }
 
 }  // namespace kv4

@@ -69,7 +69,8 @@ struct DecodeParams {
 size_t decode_workspace_bytes(int32_t batch, int32_t max_pages, int32_t num_q_heads, int32_t head_dim);
 DecodeWorkspace carve_workspace(void* base, int32_t batch, int32_t max_pages, int32_t num_q_heads,
                                 int32_t head_dim);
-hipError_t launch_decode(int fmt, const DecodeParams& p, int head_dim, hipStream_t stream);
+// phases: bit 0 work list, bit 1 attention, bit 2 merge
+hipError_t launch_decode(int fmt, const DecodeParams& p, int head_dim, unsigned phases, hipStream_t stream);
 
 hipError_t launch_probe(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream);
 int32_t probe_blocks();

@@ -119,6 +119,20 @@ def test_host_argument_errors_return_before_launch(lib):
     assert _call_decode(lib, plain, kv4.CacheDesc(fake, 10, None, 0), batch, ws_bytes=16) == -3
     assert lib.kv8_decode_attention(ctypes.byref(good), ctypes.byref(kv4.CacheDesc(fake, 10, None, 0)),
                                     ctypes.byref(batch), fake, 1.0, fake, None, fake, 16, None) == -3
+    # phased decode: the mask must select 1..7; a plan alone needs no cache, q or out
+    for ph in (0, 8, 0xFFFFFFFF):
+        assert lib.kv4_decode_phases(ctypes.byref(good), ctypes.byref(cache), ctypes.byref(batch), fake, 1.0,
+                                     fake, None, fake, 1 << 40, ph, None) == -1
+    assert lib.kv4_decode_phases(ctypes.byref(good), None, ctypes.byref(batch), None, 1.0, None, None, fake,
+                                 16, 1, None) == -3
+    assert lib.kv4_decode_phases(ctypes.byref(good), None, ctypes.byref(batch), None, 1.0, None, None, fake,
+                                 1 << 40, 2, None) == -1                       # attend needs the cache
+    assert lib.kv4_decode_phases(ctypes.byref(good), ctypes.byref(cache), ctypes.byref(batch), None, 1.0,
+                                 fake, None, fake, 1 << 40, 2, None) == -1      # attend needs q
+    assert lib.kv4_decode_phases(ctypes.byref(good), ctypes.byref(cache), ctypes.byref(batch), fake, 1.0,
+                                 None, None, fake, 1 << 40, 4, None) == -1      # merge needs out
+    assert lib.kv8_decode_phases(ctypes.byref(good), None, ctypes.byref(kv4.BatchDesc(fake, 4, fake, None, 0)),
+                                 None, 1.0, None, None, None, 0, 1, None) == 0  # empty batch
     # probe
     assert lib.kv4_hbm_read_probe(fake, 17, fake, None) == -1
     assert lib.kv4_hbm_read_probe(None, 16, fake, None) == -1

@@ -1,0 +1,48 @@
+"""Phased decode through the C ABI: PLAN once, then ATTEND + MERGE for two
+layers that share the page table and seq_lens, must give the same bits as a
+full decode call per layer; and the phased result passes the oracle check."""
+import numpy as np
+import pytest
+
+import parity_util as pu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("fmt", [0, 1, 2], ids=["kv4", "kv8", "bf16"])
+def test_plan_reused_across_layers(kv4, fmt):
+    import torch
+
+    from harness import build_config
+
+    layers = [build_config(1, fmt, layer=l, keep_inputs=(l == 1)) for l in (0, 1)]
+    for wl in layers:
+        wl.step_append()
+    assert np.array_equal(layers[0].lengths, layers[1].lengths)
+    refs = []
+    for wl in layers:
+        wl.decode()
+        torch.cuda.synchronize()
+        refs.append((wl.out.clone(), wl.lse.clone()))
+    ws = torch.empty_like(layers[0].workspace)
+    ws.fill_(0xA5)  # the plan must not depend on earlier workspace contents
+    w0 = layers[0]
+    kv4.decode_phases(w0.cache, w0.batch, None, None, None, ws, kv4.PHASE_PLAN)
+    for wl, (ref_out, ref_lse) in zip(layers, refs):
+        out = torch.full_like(wl.out, float("nan"))
+        lse = torch.full_like(wl.lse, float("nan"))
+        kv4.decode_phases(wl.cache, wl.batch, wl.q, out, lse, ws, kv4.PHASE_ATTEND)
+        kv4.decode_phases(wl.cache, wl.batch, wl.q, out, lse, ws, kv4.PHASE_MERGE)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref_out.view(torch.int16))
+        assert torch.equal(lse.view(torch.int32), ref_lse.view(torch.int32))
+    # the second layer's phased output against the oracle on a sample
+    wl = layers[1]
+    wl.out.copy_(out)
+    wl.lse.copy_(lse)
+    sample = np.random.default_rng(5).choice(wl.lengths.size, size=16, replace=False)
+    ocache, pt, lens = pu.oracle_cache_for(wl, np.sort(sample))
+    m = pu.decode_metrics(wl, np.sort(sample), ocache, pt, lens)
+    print(f"\nphased layer-1 parity fmt={fmt}: rel_l2={m['rel_l2']:.3e} max_abs={m['max_abs']:.3e} "
+          f"lse={m['lse_abs']:.3e}", flush=True)
+    pu.assert_within(m)
