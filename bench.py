@@ -195,6 +195,20 @@ def cpu_baseline(wl, budget_s=12.0, max_seqs=256):
                       f"token each + fp64 decode, {threads} OpenMP threads"}
 
 
+def copy_calibration(nbytes=1 << 30):
+    """A plain copy kernel of known size: each launch reads and writes
+    `nbytes`, so FETCH_SIZE / WRITE_SIZE of its dispatches give the factor from
+    counter KiB to HBM bytes."""
+    import torch
+
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_per_launch": nbytes, "launches": 3}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -202,10 +216,15 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--variants", action="store_true", help="also time kv8 / bf16 / plain INT4")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy 3 times (scales the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
 
     import torch
 
