@@ -195,6 +195,30 @@ def cpu_baseline(wl, budget_s=12.0, max_seqs=256):
                       f"token each + fp64 decode, {threads} OpenMP threads"}
 
 
+def read_probe_gbs(nbytes=4 << 30, reps=5):
+    """Achievable streaming read bandwidth: kv4_hbm_read_probe over `nbytes`
+    (128-bit loads, the same load width as the decode), HIP events."""
+    import torch
+
+    import int4_kv_cache_amd as kv4
+
+    buf = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(kv4.probe_blocks(), dtype=torch.int32, device="cuda")
+    for _ in range(2):
+        kv4.hbm_read_probe(buf, sink)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        kv4.hbm_read_probe(buf, sink)
+    e1.record()
+    torch.cuda.synchronize()
+    gbs = nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del buf, sink
+    torch.cuda.empty_cache()
+    return gbs
+
+
 def copy_calibration(nbytes=1 << 30):
     """A plain copy kernel of known size: each launch reads and writes
     `nbytes`, so FETCH_SIZE / WRITE_SIZE of its dispatches give the factor from
@@ -209,6 +233,87 @@ def copy_calibration(nbytes=1 << 30):
     print(json.dumps({"copy_bytes_per_launch": nbytes, "launches": 3}), flush=True)
 
 
+def run_layers(args):
+    """The 36-layer decode step (config 3): one plan, then attend + merge for
+    every layer (each its own INT4 pool and INT8 side cache), timed with HIP
+    events around each phase.  Prints one JSON line."""
+    import torch
+
+    import int4_kv_cache_amd as kv4
+    from harness import build_layers
+
+    kv4.load()
+    torch.cuda.set_device(0)
+    print("[bench] building config 3 (36 layers) ...", file=sys.stderr, flush=True)
+    t = time.time()
+    wl = build_layers(3, kv4.FMT_KV4,
+                      progress=lambda l: print(f"[bench] layer {l} built", file=sys.stderr, flush=True))
+    print(f"[bench] built in {time.time() - t:.1f} s", file=sys.stderr, flush=True)
+    stream = torch.cuda.current_stream()
+    nl = wl.n_layers
+    for _ in range(args.warmup):
+        wl.step()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2 + 2 * nl)] for _ in range(args.steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for e in ev:
+        e[0].record(stream)
+        wl.plan()
+        e[1].record(stream)
+        for l in range(nl):
+            kv4.decode_phases(wl.caches[l], wl.batch, wl.qs[l], wl.out[l], wl.lse[l], wl.workspace,
+                              kv4.PHASE_ATTEND)
+            e[2 + 2 * l].record(stream)
+            kv4.decode_phases(wl.caches[l], wl.batch, wl.qs[l], wl.out[l], wl.lse[l], wl.workspace,
+                              kv4.PHASE_MERGE)
+            e[3 + 2 * l].record(stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    plan = np.array([e[0].elapsed_time(e[1]) for e in ev])
+    att = np.array([[(e[1] if l == 0 else e[1 + 2 * l]).elapsed_time(e[2 + 2 * l]) for l in range(nl)]
+                    for e in ev])
+    mrg = np.array([[e[2 + 2 * l].elapsed_time(e[3 + 2 * l]) for l in range(nl)] for e in ev])
+    view = wl.layer(0)
+    layer_bytes = algorithmic_bytes(view, 0)
+    att_bytes = attend_bytes(view, 0)
+    ctx = int(wl.lengths.sum())
+    att_ms = float(att.mean())
+    achieved = att_bytes / (att_ms * 1e-3) / 1e9
+    result = {
+        "metric": "KV4 decode-attention ctx tokens/s (us/step and % HBM peak alongside), Qwen3-8B shape",
+        "value": ctx / (ms * 1e-3),
+        "unit": "ctx tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int4/int8 codes x bf16 q on bf16 MFMA, fp32 accumulate, bf16 out",
+        "data": "synthetic (seeded)",
+        "config": {"workload": "qwen3-8b-36-layers-b512: 36 layers x (Hq 32 / Hkv 8 / D 128), 512 seqs, "
+                               "contexts uniform in [4096, 16600], 16 sinks + 128 recent INT8; step = one "
+                               "plan + attend/merge of all 36 layers",
+                   "global_batch": int(wl.lengths.size), "ctx_tokens": ctx, "layers": nl,
+                   "plan_us": float(plan.mean()) * 1e3, "attend_us_per_layer": att_ms * 1e3,
+                   "merge_us_per_layer": float(mrg.mean()) * 1e3,
+                   "step_hbm_frac": nl * layer_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                   "step_algorithmic_bytes": nl * layer_bytes,
+                   "resident_gb": sum(c.pages.numel() + (c.side.numel() if c.side is not None else 0)
+                                      for c in wl.caches) / 1e9},
+        "hbm_read_probe_gbs": read_probe_gbs(),
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "attention_kernel<kv4, 128> (the ATTEND phase), mean over the 36 layers",
+                     "algorithmic_bytes": att_bytes},
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -216,6 +321,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--variants", action="store_true", help="also time kv8 / bf16 / plain INT4")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--config", type=int, default=CFG_IDX, choices=(2, 3),
+                    help="2: one Qwen3-8B-shaped layer, B=1024 (the default line); 3: the 36-layer "
+                         "decode step at B=512 (about 226 GB resident)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy 3 times (scales the HBM byte counters)")
     args = ap.parse_args()
@@ -224,6 +332,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.config == 3:
+        run_layers(args)
         return
 
     import torch
@@ -264,6 +375,7 @@ def main():
                    "decode_us_median": float(np.median(ph["decode"])) * 1e3,
                    "decode_hbm_frac": abytes / (us["decode"] * 1e-6) / 1e9 / HBM_PEAK_GBS,
                    "decode_algorithmic_bytes": abytes},
+        "hbm_read_probe_gbs": read_probe_gbs(),
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(),
                      "kernel": "attention_kernel<kv4, 128> (the ATTEND phase)",

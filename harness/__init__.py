@@ -8,5 +8,7 @@ from .device import (  # noqa: F401
     GpuWorkload,
     build_from_host,
     build_config,
+    build_layers,
+    MultiLayerWorkload,
     ORACLE_FMT,
 )

@@ -216,3 +216,156 @@ def build_config(cfg_idx, fmt, layer=0, n_sink=None, n_recent=None, device="cuda
     wl.tokens = tokens
     torch.cuda.synchronize()
     return wl
+
+
+# ------------------------------------------------------------ many layers --
+@dataclass
+class LayerView:
+    """One layer of a MultiLayerWorkload, with the attributes GpuWorkload has
+    for the parity helpers (layout, cache, lengths, out, lse, host rebuild)."""
+    parent: "MultiLayerWorkload"
+    index: int
+
+    def __getattr__(self, name):
+        if name in ("cfg", "fmt", "layout", "alloc", "lengths", "batch", "workspace"):
+            return getattr(self.parent, name)
+        raise AttributeError(name)
+
+    @property
+    def cache(self):
+        return self.parent.caches[self.index]
+
+    @property
+    def q(self):
+        return self.parent.qs[self.index]
+
+    @property
+    def out(self):
+        return self.parent.out[self.index]
+
+    @property
+    def lse(self):
+        return self.parent.lse[self.index]
+
+    @property
+    def tokens(self):
+        return {"slots": None}
+
+    def host_tokens(self, b: int):
+        return self.parent.host_tokens(self.index, b)
+
+    def host_q(self):
+        import torch
+
+        return self.q.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+@dataclass
+class MultiLayerWorkload:
+    """A decode step over many layers: one page table, seq_lens and plan for
+    the batch; per layer its own cache (pages + side), q, out and lse."""
+    cfg: object
+    fmt: int
+    layout: kv4.Layout
+    alloc: PageAllocator
+    lengths: np.ndarray
+    batch: kv4.Batch
+    caches: list
+    qs: list
+    out: object                      # bf16 [layers][B][Hq][D]
+    lse: object                      # fp32 [layers][B][Hq]
+    workspace: object
+    chunks: np.ndarray               # sequence boundaries of the draw chunks
+    _host: Dict = field(default_factory=dict)
+
+    @property
+    def n_layers(self) -> int:
+        return len(self.caches)
+
+    def layer(self, l: int) -> LayerView:
+        return LayerView(self, l)
+
+    def plan(self, stream=None):
+        c = self.caches[0]
+        kv4.decode_phases(c, self.batch, None, None, None, self.workspace, kv4.PHASE_PLAN,
+                          stream=stream)
+
+    def attend_layer(self, l: int, stream=None):
+        kv4.decode_phases(self.caches[l], self.batch, self.qs[l], self.out[l], self.lse[l], self.workspace,
+                          kv4.PHASE_ATTEND | kv4.PHASE_MERGE, stream=stream)
+
+    def step(self, stream=None):
+        """The decode of every layer: one plan, then attend + merge per layer."""
+        self.plan(stream)
+        for l in range(self.n_layers):
+            self.attend_layer(l, stream)
+
+    def _chunk_of(self, b: int) -> int:
+        return int(np.searchsorted(self.chunks, b, side="right") - 1)
+
+    def host_tokens(self, l: int, b: int):
+        """bf16 bits K, V [L_b][Hkv][D] of sequence b in layer l, redrawn on the
+        device from the chunk's seed (the draws are not kept)."""
+        key = (l, b)
+        if key not in self._host:
+            c = self._chunk_of(b)
+            s, e = int(self.chunks[c]), int(self.chunks[c + 1])
+            off = np.concatenate([[0], np.cumsum(self.lengths[s:e].astype(np.int64))])
+            k, v = device_tokens(self.cfg, l, 100 + c, int(off[-1]), self.caches[l].pages.device)
+            import torch
+
+            for bb in range(s, e):
+                if (l, bb) in self._wanted or bb == b:
+                    lo, hi = int(off[bb - s]), int(off[bb - s + 1])
+                    self._host[(l, bb)] = (k[lo:hi].view(torch.int16).cpu().numpy().view(np.uint16),
+                                           v[lo:hi].view(torch.int16).cpu().numpy().view(np.uint16))
+            del k, v
+        return self._host.pop(key)
+
+    _wanted: set = field(default_factory=set)
+
+    def want(self, l: int, sample):
+        """Announce the sequences of layer l that host_tokens will be asked for,
+        so one redraw of a chunk serves all of them."""
+        for b in sample:
+            self._wanted.add((l, int(b)))
+
+
+def build_layers(cfg_idx, fmt, n_layers=None, device="cuda", chunk_seqs=32, n_sink=None, n_recent=None,
+                 progress=None):
+    """Many-layer workload: every layer's cache is built with device draws,
+    chunk by chunk of sequences (so the bf16 draws of a whole layer are never
+    resident at once); all L tokens of every sequence are appended."""
+    import torch
+
+    cfg = get_config(cfg_idx)
+    L = int(cfg.layers if n_layers is None else n_layers)
+    lengths = np.asarray(context_lengths(cfg), dtype=np.int32)
+    B = lengths.size
+    layout = _layout(cfg, fmt, n_sink, n_recent)
+    alloc = PageAllocator(lengths, seed=cfg.seed)
+    pt = _i32(alloc.page_table, device)
+    sl = _i32(lengths, device)
+    chunks = np.arange(0, B + chunk_seqs, chunk_seqs)
+    chunks[-1] = B
+    chunks = np.unique(chunks)
+    caches, qs = [], []
+    for l in range(L):
+        cache = kv4.alloc_cache(fmt, layout, alloc.num_pages, B, device)
+        for c in range(len(chunks) - 1):
+            s, e = int(chunks[c]), int(chunks[c + 1])
+            off = np.concatenate([[0], np.cumsum(lengths[s:e].astype(np.int64))])
+            k, v = device_tokens(cfg, l, 100 + c, int(off[-1]), device)
+            bt = kv4.Batch(pt[s:e], sl[s:e], _i32(np.arange(s, e), device))
+            kv4.append(cache, bt, k, v, _i32(off, device))
+            del k, v
+        caches.append(cache)
+        qs.append(device_queries(cfg, l, B, device))
+        torch.cuda.synchronize()
+        if progress:
+            progress(l)
+    out = torch.zeros((L, B, cfg.num_q_heads, cfg.head_dim), dtype=torch.bfloat16, device=device)
+    lse = torch.zeros((L, B, cfg.num_q_heads), dtype=torch.float32, device=device)
+    ws = torch.empty(kv4.workspace_bytes(layout, B, alloc.max_pages), dtype=torch.uint8, device=device)
+    return MultiLayerWorkload(cfg, fmt, layout, alloc, lengths, kv4.Batch(pt, sl), caches, qs, out, lse, ws,
+                              chunks)
