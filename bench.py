@@ -87,12 +87,18 @@ KERNEL_SOURCES = [os.path.join(ROOT, "int4_kv_cache_amd", "csrc", f)
 
 
 def kernel_source_hash():
+    """sha256 of the kernel sources with comments and blank space removed, so
+    an edit of a comment does not discard a measurement of the same code."""
     import hashlib
+    import re
 
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(f, "rb") as fh:
-            h.update(fh.read())
+        with open(f) as fh:
+            src = fh.read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", " ", src)
+        h.update(" ".join(src.split()).encode())
     return h.hexdigest()
 
 

@@ -523,7 +523,7 @@ __device__ inline void write_item(const DecodeParams& p, uint32_t pos, int b, co
 // One workgroup: chooses the chunk size from the total work, numbers the
 // partial slots of split sequences and writes the item descriptors: all full
 // chunks first, then the remaining (shorter) items in decreasing size, so the
-// dynamic schedule ends on small items.
+// round-robin assignment of units to waves ends on small items.
 __global__ __launch_bounds__(1024) void worklist_kernel(DecodeParams p, int units_per_item) {
   __shared__ unsigned long long total_pages;
   __shared__ int chunk_sh;
