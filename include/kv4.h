@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define KV4_ABI_VERSION 1
+#define KV4_ABI_VERSION 2
 
 typedef enum {
   KV4_OK = 0,
@@ -71,7 +71,12 @@ typedef enum {
  * num_q_heads a multiple of num_kv_heads, n_sink >= 0, n_recent >= 0 and
  * n_sink + n_recent <= 144 (the bound on the protected set, [NEWS]
  * Interpretation para 3).  n_sink = n_recent = 0 is plain INT4 KV.  The kv8_
- * and kvbf16_ entry points ignore n_sink / n_recent. */
+ * and kvbf16_ entry points ignore n_sink / n_recent.
+ * flags: 0, or KV4_LAYOUT_WIDE_PROTECTION, which lifts the bound to
+ * n_sink + n_recent <= 4096 -- for studies of wider protection than the
+ * method's; the kernels are the same.  Other bits: KV4_ERR_INVALID_ARG. */
+#define KV4_LAYOUT_WIDE_PROTECTION 1u
+#define KV4_WIDE_PROTECTION_MAX 4096
 typedef struct {
   int32_t num_q_heads;
   int32_t num_kv_heads;
@@ -80,6 +85,7 @@ typedef struct {
   int32_t group_size;
   int32_t n_sink;
   int32_t n_recent;
+  uint32_t flags;
 } kv4_layout;
 
 /* Cache storage (host struct of device pointers). */

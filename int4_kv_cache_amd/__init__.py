@@ -34,7 +34,10 @@ class Layout(ctypes.Structure):
     _fields_ = [("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("page_size", ctypes.c_int32),
                 ("group_size", ctypes.c_int32), ("n_sink", ctypes.c_int32),
-                ("n_recent", ctypes.c_int32)]
+                ("n_recent", ctypes.c_int32), ("flags", ctypes.c_uint32)]
+
+
+LAYOUT_WIDE_PROTECTION = 1  # lifts the n_sink + n_recent <= 144 bound to 4096
 
 
 class CacheDesc(ctypes.Structure):
@@ -118,8 +121,11 @@ def _stream(stream=None) -> int:
 
 
 def make_layout(num_q_heads, num_kv_heads, head_dim, n_sink, n_recent, page_size=16,
-                group_size=32) -> Layout:
-    return Layout(num_q_heads, num_kv_heads, head_dim, page_size, group_size, n_sink, n_recent)
+                group_size=32, flags=None) -> Layout:
+    """flags None: KV4_LAYOUT_WIDE_PROTECTION exactly when n_sink + n_recent > 144."""
+    if flags is None:
+        flags = LAYOUT_WIDE_PROTECTION if n_sink + n_recent > 144 else 0
+    return Layout(num_q_heads, num_kv_heads, head_dim, page_size, group_size, n_sink, n_recent, flags)
 
 
 def block_bytes(fmt: int, layout: Layout) -> int:

@@ -25,7 +25,9 @@ kv4_status layout_check(const kv4_layout* L, int fmt) {
   if (L->page_size != 16 || L->group_size != 32) return KV4_ERR_UNSUPPORTED;
   const int g = L->num_q_heads / L->num_kv_heads;
   if (g != 1 && g != 2 && g != 4 && g != 8) return KV4_ERR_UNSUPPORTED;
-  if (fmt == kFmtKV4 && L->n_sink + L->n_recent > kv4::kMaxProtected) return KV4_ERR_INVALID_ARG;
+  if (L->flags & ~KV4_LAYOUT_WIDE_PROTECTION) return KV4_ERR_INVALID_ARG;
+  const int max_prot = (L->flags & KV4_LAYOUT_WIDE_PROTECTION) ? KV4_WIDE_PROTECTION_MAX : kv4::kMaxProtected;
+  if (fmt == kFmtKV4 && int64_t(L->n_sink) + L->n_recent > max_prot) return KV4_ERR_INVALID_ARG;
   return KV4_OK;
 }
 

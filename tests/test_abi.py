@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.kv4_abi_version() == 1
+    assert lib.kv4_abi_version() == 2
     for code, text in kv4.STATUS.items():
         assert lib.kv4_status_string(code).decode() == text
     assert lib.kv4_status_string(12345).decode() == "unknown status"
@@ -81,7 +81,9 @@ def test_host_argument_errors_return_before_launch(lib):
     # bad layouts
     for lay, want in [(kv4.make_layout(32, 7, 128, 16, 128), -1),    # Hq % Hkv
                       (kv4.make_layout(32, 8, 96, 16, 128), -2),     # head_dim
-                      (kv4.make_layout(32, 8, 128, 16, 129), -1),    # S + R > 144
+                      (kv4.make_layout(32, 8, 128, 16, 129, flags=0), -1),    # S + R > 144
+                      (kv4.make_layout(32, 8, 128, 16, 4081), -1),   # > 4096 even when widened
+                      (kv4.make_layout(32, 8, 128, 16, 128, flags=2), -1),    # unknown flag
                       (kv4.make_layout(32, 8, 128, -1, 0), -1),
                       (kv4.make_layout(32, 8, 128, 16, 128, page_size=32), -2),
                       (kv4.make_layout(32, 8, 128, 16, 128, group_size=64), -2),
@@ -103,6 +105,11 @@ def test_host_argument_errors_return_before_launch(lib):
     for sm in (0.0, -1.0, float("inf"), float("nan")):
         assert lib.kv4_decode_attention(ctypes.byref(good), ctypes.byref(cache), ctypes.byref(batch), fake,
                                         sm, fake, None, fake, 1 << 40, None) == -1
+    # wider protection is accepted behind the flag (then the workspace check is reached)
+    wide = kv4.make_layout(32, 8, 128, 32, 480)
+    assert wide.flags == kv4.LAYOUT_WIDE_PROTECTION
+    assert _call_decode(lib, wide, cache, batch, ws_bytes=16) == -3
+    assert kv4.side_bytes(wide) == 32 * (32 * 128 + 64)
     # workspace too small
     assert _call_decode(lib, good, cache, batch, ws_bytes=16) == -3
     # append argument errors
