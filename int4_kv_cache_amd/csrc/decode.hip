@@ -415,8 +415,8 @@ __device__ inline void step(Unit<D>& u, const Tile<KIND, D>& T0, const Tile<KIND
 // (past the end it re-reads the last step, which the L2 holds) so the loop
 // body has one fixed load sequence and each wait covers exactly the step it
 // needs.  Tile n (odd n) is a masked copy of tile n-1.
-template <int KIND, int D, int STAGES, class PtrFn, class MaskFn>
-__device__ inline void run_tiles(Unit<D>& u, int n, PtrFn ptr, MaskFn mask, int lane) {
+template <int KIND, int D, int STAGES, class PtrFn, class MaskFn, class SetupFn>
+__device__ inline void run_tiles(Unit<D>& u, int n, PtrFn ptr, MaskFn mask, int lane, SetupFn setup) {
   if (n <= 0) return;
   const LaneOff<KIND, D> off(lane & 15, lane >> 4);
   const int nsteps = (n + 1) >> 1;
@@ -435,11 +435,13 @@ __device__ inline void run_tiles(Unit<D>& u, int n, PtrFn ptr, MaskFn mask, int 
     for (int s = 0; s < nsteps; ++s) {
       Tile<KIND, D> a0, a1;
       load(a0, a1, s);
+      setup();
       run(a0, a1, s);
     }
   } else if constexpr (STAGES == 2) {
     Tile<KIND, D> a0, a1, b0, b1;
     load(a0, a1, 0);
+    setup();
     for (int s = 0;; s += 2) {
       load(b0, b1, s + 1);
       run(a0, a1, s);
@@ -452,6 +454,7 @@ __device__ inline void run_tiles(Unit<D>& u, int n, PtrFn ptr, MaskFn mask, int 
     Tile<KIND, D> a0, a1, b0, b1, c0, c1;
     load(a0, a1, 0);
     load(b0, b1, 1);
+    setup();
     for (int s = 0;; s += 3) {
       load(c0, c1, s + 2);
       run(a0, a1, s);
@@ -707,41 +710,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KV4_WAVES_P
     const int b = d.b, L = d.L;
     const Regions g = regions(L, S, R);
 
-    // ---- unit set-up: q operand of this lane's row (head hl, group grp)
+    // ---- unit set-up.  The q loads are issued here, but the q operand is
+    // built only after the unit's first tile loads are in flight (run_tiles
+    // calls `setup` after its prologue), so the q latency overlaps them.
     Unit<D> u;
+    uint4 qraw[NG];
+    bool pending = true;
     {
       const int hl = ln / NG, grp = ln % NG;
       const int j = hb * HB + hl;
       const bool valid = j < G;
+      // lanes whose k-slice is the row's group hold q (all of the group's
+      // channels between them); the others hold zeros
       const bool take = valid && ((NG == 4 ? kg : (kg >> 1)) == grp);
       const uint16_t* qrow = p.q + (int64_t(b) * Hq + h * G + (valid ? j : 0)) * D;
 #pragma unroll
       for (int t = 0; t < NG; ++t) {
-        uint32_t w0 = 0, w1 = 0, w2 = 0, w3 = 0;
-        if (take) {
-          const uint4 a = *reinterpret_cast<const uint4*>(qrow + kg * (D / 4) + 8 * t);
-          w0 = a.x; w1 = a.y; w2 = a.z; w3 = a.w;
-        }
-        if constexpr (MAIN == kBf16Page) {
-          u.bq[t] = bf8(w0, w1, w2, w3);  // channels in natural order
-        } else {
-          // element pairs (c, c+4): the order the code conversions produce
-          u.bq[t] = bf8(__builtin_amdgcn_perm(w2, w0, 0x05040100u), __builtin_amdgcn_perm(w2, w0, 0x07060302u),
-                        __builtin_amdgcn_perm(w3, w1, 0x05040100u), __builtin_amdgcn_perm(w3, w1, 0x07060302u));
-        }
+        qraw[t] = make_uint4(0u, 0u, 0u, 0u);
+        if (take) qraw[t] = *reinterpret_cast<const uint4*>(qrow + kg * (D / 4) + 8 * t);
       }
-      double qs = 0.0;
-      if (MAIN == kInt4Page && valid) {
-        const uint4* qg = reinterpret_cast<const uint4*>(qrow + grp * 32);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint4 a = qg[i];
-          const uint32_t w[4] = {a.x, a.y, a.z, a.w};
-#pragma unroll
-          for (int k = 0; k < 4; ++k) qs += double(bf16_lo(w[k])) + double(bf16_hi(w[k]));
-        }
-      }
-      u.qsum = float(qs);
 #pragma unroll
       for (int t = 0; t < NT; ++t) u.o[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       u.corr = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -749,6 +736,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KV4_WAVES_P
       u.l = 0.f;
       u.qk_scale = p.softmax_scale * kLog2e;
     }
+    auto setup = [&]() {
+      if (!pending) return;
+      pending = false;
+      float qs = 0.f;
+#pragma unroll
+      for (int t = 0; t < NG; ++t) {
+        const uint32_t w0 = qraw[t].x, w1 = qraw[t].y, w2 = qraw[t].z, w3 = qraw[t].w;
+        if constexpr (MAIN == kBf16Page) {
+          u.bq[t] = bf8(w0, w1, w2, w3);  // channels in natural order
+        } else {
+          // element pairs (c, c+4): the order the code conversions produce
+          u.bq[t] = bf8(__builtin_amdgcn_perm(w2, w0, 0x05040100u), __builtin_amdgcn_perm(w2, w0, 0x07060302u),
+                        __builtin_amdgcn_perm(w3, w1, 0x05040100u), __builtin_amdgcn_perm(w3, w1, 0x07060302u));
+          qs += ((bf16_lo(w0) + bf16_hi(w0)) + (bf16_lo(w1) + bf16_hi(w1))) +
+                ((bf16_lo(w2) + bf16_hi(w2)) + (bf16_lo(w3) + bf16_hi(w3)));
+        }
+      }
+      // the row's sum of q over its group: the other lanes of the row hold 0
+      qs += __shfl_xor(qs, 16, kWave);
+      qs += __shfl_xor(qs, 32, kWave);
+      u.qsum = qs;
+    };
 
     // ---- protected rows: INT8 side-cache tiles (sinks, then the ring)
     if (FMT == kFmtKV4 && d.ck == 0 && L > 0 && S + R > 0 && d.slot >= 0 && d.slot < p.num_slots) {
@@ -762,7 +771,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KV4_WAVES_P
         const int r0 = i * kPage;
         return range_mask(0 - r0, se - r0) | range_mask(S - r0, S + nring - r0);
       };
-      run_tiles<kInt8Tile, D, KV4_STAGES8>(u, ntiles, ptr, mask, lane);
+      run_tiles<kInt8Tile, D, KV4_STAGES8>(u, ntiles, ptr, mask, lane, setup);
     }
 
     // ---- middle pages of this item (at most 64: one page id per lane)
@@ -777,7 +786,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KV4_WAVES_P
         return pid < 0 ? 0u : range_mask(g.mb - p0, g.me - p0);
       };
       run_tiles<MAIN, D, MAIN == kInt4Page ? KV4_STAGES : (MAIN == kInt8Tile ? KV4_STAGES8 : 1)>(u, d.npg, ptr,
-                                                                                                   mask, lane);
+                                                                                                   mask, lane, setup);
     }
 
     // ---- finish: per-head denominators, then output or partial
