@@ -181,6 +181,9 @@ kv4_status kv4_decode_workspace_size(const kv4_layout* layout, int32_t batch,
  *   out    bf16 [batch][num_q_heads][head_dim] (rounded to nearest even)
  *   lse    fp32 [batch][num_q_heads] natural-log sum of exp, or NULL
  * softmax_scale must be positive and finite (KV4_ERR_INVALID_ARG otherwise).
+ * KV4_ERR_UNSUPPORTED if batch x ceil(max_pages / 32) x num_kv_heads x
+ * ceil(num_q_heads / num_kv_heads / (2048 / head_dim)) reaches 2^31 (the
+ * work units are numbered in 32 bits).
  * L = 0 gives out = 0 and lse = -inf.  Arithmetic: exact dequantized
  * products, fp32 accumulation.  The workspace is scratch for this call
  * (PLAN + ATTEND + MERGE of kv4_decode_phases). */

@@ -111,6 +111,8 @@ kv4_status decode_impl(int fmt, const kv4_layout* L, const kv4_cache* c, const k
   if ((phases & (KV4_PHASE_ATTEND | KV4_PHASE_MERGE)) && !out) return KV4_ERR_INVALID_ARG;
   if ((phases & KV4_PHASE_ATTEND) && !q) return KV4_ERR_INVALID_ARG;
   if (!(sm > 0.0f) || sm > 3.0e38f) return KV4_ERR_INVALID_ARG;  // positive and finite
+  if (!kv4::decode_units_fit(b->batch, b->max_pages, L->num_q_heads, L->num_kv_heads, L->head_dim))
+    return KV4_ERR_UNSUPPORTED;
   const size_t need = kv4::decode_workspace_bytes(b->batch, b->max_pages, L->num_q_heads, L->head_dim);
   if (ws_bytes < need) return KV4_ERR_WORKSPACE;
   kv4::DecodeParams p{};

@@ -644,7 +644,7 @@ struct RawItem {
 
 __device__ inline int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
-__device__ inline RawItem load_item(const DecodeParams& p, int64_t item) {
+__device__ inline RawItem load_item(const DecodeParams& p, uint32_t item) {
   return RawItem{p.ws.items[2 * item], p.ws.items[2 * item + 1]};
 }
 
@@ -674,7 +674,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KV4_WAVES_P
   const int UPI = H * NHB;  // units per item
   const int S = FMT == kFmtKV4 ? p.n_sink : 0;
   const int R = FMT == kFmtKV4 ? p.n_recent : 0;
-  const int64_t units = int64_t(p.ws.header[1]) * UPI;
+  // unit indices fit 32 bits: the host bounds the work list (items x units per item < 2^31)
+  const uint32_t units = p.ws.header[1] * uint32_t(UPI);
   if (units == 0) return;
 
   // Static round robin over the list (longest items first): in round k the
@@ -683,8 +684,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KV4_WAVES_P
   // rows open, and neighbouring waves have units of about the same size.  The
   // next units are known in advance: the descriptor of unit k+2 and the page
   // ids of unit k+1 are loaded when unit k starts.
-  const int64_t nw = int64_t(gridDim.x) * (blockDim.x / kWave);
-  auto item_of = [&](int64_t t) -> int64_t { return (t < units ? t : units - 1) / UPI; };
+  const uint32_t nw = gridDim.x * (blockDim.x / kWave);
+  auto item_of = [&](uint32_t t) -> uint32_t { return (t < units ? t : units - 1) / uint32_t(UPI); };
   auto fetch_pids = [&](const ItemDesc& d) -> int {
     int v = 0;
     if (lane < d.npg) {
@@ -693,7 +694,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KV4_WAVES_P
     }
     return v;
   };
-  int64_t t0 = int64_t(blockIdx.x) * (blockDim.x / kWave) + uniform(threadIdx.x / kWave);
+  uint32_t t0 = blockIdx.x * (blockDim.x / kWave) + uniform(threadIdx.x / kWave);
   ItemDesc d0 = decode_item(load_item(p, item_of(t0)));
   RawItem r1 = load_item(p, item_of(t0 + nw));
   int pid0 = fetch_pids(d0);
@@ -704,7 +705,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KV4_WAVES_P
     const ItemDesc d1 = decode_item(r1);
     const int pid1 = fetch_pids(d1);
 
-    const int rem = int(t0 % UPI);
+    const int rem = int(t0 % uint32_t(UPI));
     const int h = rem / NHB, hb = rem % NHB;
     const ItemDesc d = d0;
     const int b = d.b, L = d.L;
@@ -953,6 +954,14 @@ static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 static int64_t max_items_of(int32_t batch, int32_t max_pages) {
   const int64_t per_seq = (int64_t(max_pages) + kChunkPages - 1) / kChunkPages;
   return int64_t(batch) * (per_seq < 1 ? 1 : per_seq);
+}
+
+bool decode_units_fit(int32_t batch, int32_t max_pages, int32_t num_q_heads, int32_t num_kv_heads,
+                      int32_t head_dim) {
+  const int64_t hb = 16 / (head_dim / 32);
+  const int64_t g = num_q_heads / num_kv_heads;
+  const int64_t units = max_items_of(batch, max_pages) * num_kv_heads * ((g + hb - 1) / hb);
+  return units < (int64_t(1) << 31);
 }
 
 size_t decode_workspace_bytes(int32_t batch, int32_t max_pages, int32_t num_q_heads, int32_t head_dim) {

@@ -67,6 +67,9 @@ struct DecodeParams {
 };
 
 size_t decode_workspace_bytes(int32_t batch, int32_t max_pages, int32_t num_q_heads, int32_t head_dim);
+// whether the batch's work units can be numbered in 32 bits
+bool decode_units_fit(int32_t batch, int32_t max_pages, int32_t num_q_heads, int32_t num_kv_heads,
+                      int32_t head_dim);
 DecodeWorkspace carve_workspace(void* base, int32_t batch, int32_t max_pages, int32_t num_q_heads,
                                 int32_t head_dim);
 // phases: bit 0 work list, bit 1 attention, bit 2 merge
