@@ -14,12 +14,20 @@
 namespace kv4 {
 namespace {
 
-// Largest b with cu[b] <= t (cu non-decreasing, cu[0] = 0 <= t < cu[batch]).
-__device__ inline int find_seq(const int32_t* __restrict__ cu, int batch, int t) {
+// Largest b with cu[b] <= t (cu non-decreasing, cu[0] = 0 <= t < cu[batch]),
+// searched by the whole wave: each round the 64 lanes probe evenly spaced
+// entries of the current bracket, which shrinks it 64-fold (two rounds for
+// 4096 sequences) instead of halving it per dependent load.
+__device__ inline int find_seq(const int32_t* __restrict__ cu, int batch, int t, int lane) {
   int lo = 0, hi = batch;  // invariant: cu[lo] <= t < cu[hi]
   while (hi - lo > 1) {
-    int mid = (lo + hi) >> 1;
-    if (cu[mid] <= t) lo = mid; else hi = mid;
+    const int step = (hi - lo + kWave - 1) / kWave;
+    const int idx = lo + lane * step;
+    const bool le = idx < hi && cu[idx] <= t;  // true on a prefix of the lanes, lane 0 included
+    const unsigned long long m = __ballot(le);
+    const int last = 63 - __clzll((long long)m);
+    lo = lo + last * step;
+    hi = min(hi, lo + step);
   }
   return lo;
 }
@@ -133,7 +141,16 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
   const int H = p.num_kv_heads;
   if (w >= int64_t(p.total_new) * H) return;
   const int t = int(w / H), h = int(w % H);
-  const int b = find_seq(p.cu_new, p.batch, t);
+  // the new row's values do not depend on the sequence: load them first
+  const uint16_t* kr = p.k_new + (int64_t(t) * H + h) * D + lane * E;
+  const uint16_t* vr = p.v_new + (int64_t(t) * H + h) * D + lane * E;
+  uint16_t kb[E], vb[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    kb[e] = kr[e];
+    vb[e] = vr[e];
+  }
+  const int b = find_seq(p.cu_new, p.batch, t, lane);
   const int nb = p.cu_new[b + 1] - p.cu_new[b];
   const int pos = p.seq_lens[b] - nb + (t - p.cu_new[b]);
   if (pos < 0 || pos >= p.max_pages * kPage) return;  // outside the page table: skipped
@@ -141,14 +158,9 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
   if (pid < 0 || pid >= p.num_pages) return;
   const int r = pos % kPage;
 
-  const uint16_t* kr = p.k_new + (int64_t(t) * H + h) * D + lane * E;
-  const uint16_t* vr = p.v_new + (int64_t(t) * H + h) * D + lane * E;
-  uint16_t kb[E], vb[E];
   float kf[E], vf[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    kb[e] = kr[e];
-    vb[e] = vr[e];
     kf[e] = bf16_to_f32(kb[e]);
     vf[e] = bf16_to_f32(vb[e]);
   }

@@ -523,49 +523,71 @@ __device__ inline void write_item(const DecodeParams& p, uint32_t pos, int b, co
   p.ws.items[2 * pos + 1] = make_int4(n, pbase, slot, 0);
 }
 
+// Block-wide helpers of the work-list kernel (1024 threads = 16 waves).
+// Inclusive scan of a 64-bit value within a wave.
+__device__ inline unsigned long long wave_scan_u64(unsigned long long v, int lane) {
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const uint32_t lo = __shfl_up(uint32_t(v), o, kWave), hi = __shfl_up(uint32_t(v >> 32), o, kWave);
+    if (lane >= o) v += (unsigned long long)lo | ((unsigned long long)hi << 32);
+  }
+  return v;
+}
+// Exclusive prefix of v over the block's threads and the block total (every
+// thread gets both).  `part` is a 16-entry LDS array; the call ends with a
+// barrier, so `part` may be reused right after.
+__device__ inline unsigned long long block_exclusive_scan(unsigned long long v, unsigned long long* part,
+                                                          unsigned long long& total) {
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
+  const unsigned long long inc = wave_scan_u64(v, lane);
+  if (lane == kWave - 1) part[wid] = inc;
+  __syncthreads();
+  unsigned long long before = 0ull, all = 0ull;
+  for (int i = 0; i < 16; ++i) {
+    const unsigned long long t = part[i];
+    if (i < wid) before += t;
+    all += t;
+  }
+  __syncthreads();
+  total = all;
+  return before + inc - v;
+}
+
 // One workgroup: chooses the chunk size from the total work, numbers the
 // partial slots of split sequences and writes the item descriptors: all full
 // chunks first, then the remaining (shorter) items in decreasing size, so the
-// round-robin assignment of units to waves ends on small items.
+// round-robin assignment of units to waves ends on small items.  Each
+// thread handles sequences tid, tid + 1024, ...; the first one's lengths
+// are read once and kept.
 __global__ __launch_bounds__(1024) void worklist_kernel(DecodeParams p, int units_per_item) {
-  __shared__ unsigned long long total_pages;
-  __shared__ int chunk_sh;
-  __shared__ int run_full, run_split;
-  __shared__ uint32_t nmerge;
-  __shared__ unsigned long long scan[1024];  // (split items << 32) | full items
+  __shared__ unsigned long long part[16];
   __shared__ uint32_t bucket[kMaxChunkPages + 2];
-  const int tid = threadIdx.x;
-  if (tid == 0) {
-    total_pages = 0ull;
-    run_full = 0;
-    run_split = 0;
-    nmerge = 0u;
-  }
+  __shared__ uint32_t nmerge;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
   for (int i = tid; i < kMaxChunkPages + 2; i += 1024) bucket[i] = 0u;
-  __syncthreads();
+  if (tid == 0) nmerge = 0u;
+  SeqWork w0{};
+  if (tid < p.batch) w0 = seq_work(p, tid);
   unsigned long long mine = 0ull;
   for (int b = tid; b < p.batch; b += 1024) {
-    const SeqWork w = seq_work(p, b);
+    const SeqWork w = b == tid ? w0 : seq_work(p, b);
     mine += unsigned(mid_pages(w)) + unsigned(kProtectedCost * w.prot_tiles);
   }
-  atomicAdd(&total_pages, mine);
-  __syncthreads();
-  if (tid == 0) {
-    // about 8 units per resident wave
-    const unsigned long long denom = 8ull * unsigned(p.resident_waves > 0 ? p.resident_waves : 1);
-    unsigned long long c = (total_pages * unsigned(units_per_item) + denom - 1) / denom;
-    c = c < unsigned(kChunkPages) ? unsigned(kChunkPages) : (c > unsigned(kMaxChunkPages) ? kMaxChunkPages : c);
-    chunk_sh = int(c);
-  }
-  __syncthreads();
-  const int chunk = chunk_sh;
+  unsigned long long total_pages = 0ull;
+  (void)block_exclusive_scan(mine, part, total_pages);
+  // about 8 units per resident wave
+  const unsigned long long denom = 8ull * unsigned(p.resident_waves > 0 ? p.resident_waves : 1);
+  unsigned long long cl = (total_pages * unsigned(units_per_item) + denom - 1) / denom;
+  cl = cl < unsigned(kChunkPages) ? unsigned(kChunkPages) : (cl > unsigned(kMaxChunkPages) ? kMaxChunkPages : cl);
+  const int chunk = int(cl);
 
   // pass 1: full items (scan) and the histogram of the other items' sizes
+  int run_full = 0, run_split = 0;
   for (int base = 0; base < p.batch; base += 1024) {
     const int b = base + tid;
     int full = 0, split = 0;
     if (b < p.batch) {
-      const SeqWork w = seq_work(p, b);
+      const SeqWork w = base == 0 ? w0 : seq_work(p, b);
       const int n = n_items(w, chunk);
       for (int k = 0; k < n; ++k) {
         const int pg = item_pages(w, chunk, k);
@@ -574,42 +596,35 @@ __global__ __launch_bounds__(1024) void worklist_kernel(DecodeParams p, int unit
       }
       split = n > 1 ? n : 0;
     }
-    const unsigned long long mine2 = (unsigned long long)full | ((unsigned long long)split << 32);
-    scan[tid] = mine2;
-    __syncthreads();
-    for (int o = 1; o < 1024; o <<= 1) {  // inclusive Hillis-Steele scan of two 32-bit counts
-      const unsigned long long v = tid >= o ? scan[tid - o] : 0ull;
-      __syncthreads();
-      scan[tid] += v;
-      __syncthreads();
-    }
+    unsigned long long tile = 0ull;
+    const unsigned long long ex =
+        block_exclusive_scan((unsigned long long)full | ((unsigned long long)split << 32), part, tile);
     if (b < p.batch) {
-      const unsigned long long ex = scan[tid] - mine2;
       p.ws.item_base[b] = run_split + int(ex >> 32);
       p.ws.merge_list[b] = run_full + int(ex & 0xFFFFFFFFull);  // scratch: first full-item position
     }
-    __syncthreads();
-    if (tid == 1023) {
-      run_full += int(scan[1023] & 0xFFFFFFFFull);
-      run_split += int(scan[1023] >> 32);
-    }
-    __syncthreads();
+    run_full += int(tile & 0xFFFFFFFFull);
+    run_split += int(tile >> 32);
   }
-  if (tid == 0) {
-    uint32_t acc = uint32_t(run_full);  // shorter items follow the full ones
-    for (int i = 0; i <= kMaxChunkPages; ++i) {
-      const uint32_t c = bucket[i];
-      bucket[i] = acc;
-      acc += c;
+  // positions of the shorter items, longest first (bucket i holds size
+  // kMaxChunkPages - i): an exclusive scan of the bucket counts by wave 0
+  if (wid == 0) {
+    const int i0 = 2 * lane, i1 = 2 * lane + 1;
+    const uint32_t c0 = i0 <= kMaxChunkPages ? bucket[i0] : 0u, c1 = i1 <= kMaxChunkPages ? bucket[i1] : 0u;
+    const unsigned long long inc = wave_scan_u64((unsigned long long)(c0 + c1), lane);
+    const uint32_t start = uint32_t(run_full) + uint32_t(inc) - (c0 + c1);
+    if (i0 <= kMaxChunkPages) bucket[i0] = start;
+    if (i1 <= kMaxChunkPages) bucket[i1] = start + c0;
+    if (lane == kWave - 1) {
+      p.ws.header[0] = 0u;
+      p.ws.header[1] = uint32_t(run_full) + uint32_t(inc);
+      p.ws.header[2] = uint32_t(chunk);
     }
-    p.ws.header[0] = 0u;
-    p.ws.header[1] = acc;
-    p.ws.header[2] = uint32_t(chunk);
   }
   __syncthreads();
   // pass 2: descriptors
   for (int b = tid; b < p.batch; b += 1024) {
-    const SeqWork w = seq_work(p, b);
+    const SeqWork w = b == tid ? w0 : seq_work(p, b);
     const int n = n_items(w, chunk);
     const int pbase = p.ws.item_base[b];
     uint32_t fpos = uint32_t(p.ws.merge_list[b]);
@@ -622,8 +637,10 @@ __global__ __launch_bounds__(1024) void worklist_kernel(DecodeParams p, int unit
   }
   __syncthreads();
   // list of split sequences for the merge (overwrites the scratch use above)
-  for (int b = tid; b < p.batch; b += 1024)
-    if (p.ws.item_count[b] > 1) p.ws.merge_list[atomicAdd(&nmerge, 1u)] = b;
+  for (int b = tid; b < p.batch; b += 1024) {
+    const SeqWork w = b == tid ? w0 : seq_work(p, b);
+    if (n_items(w, chunk) > 1) p.ws.merge_list[atomicAdd(&nmerge, 1u)] = b;
+  }
   __syncthreads();
   if (tid == 0) p.ws.header[3] = nmerge;
 }
@@ -837,12 +854,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KV4_WAVES_P
 }
 
 // ----------------------------------------------------------------- merge ---
-// Exact log-sum-exp merge of the partials of split sequences; a persistent
-// grid strides over (split sequence, query head) pairs.  The lanes first read
-// the (m, l) of all items at once, then the output channels are combined.
+// Exact log-sum-exp merge of the partials of split sequences ([NEWS]
+// Interpretation para 3); a persistent grid strides over (split sequence,
+// query head) pairs.  Items are taken eight at a time: the (m, l) of the eight
+// (one per lane) and their output channels are loaded together, so a
+// sequence of up to eight items costs one memory round trip.
 template <int D>
 __global__ __launch_bounds__(256) void merge_kernel(DecodeParams p) {
-  constexpr int E = D / kWave;
+  constexpr int E = D / kWave;  // output channels per lane
+  constexpr int K = 8;          // items per round
   const int lane = threadIdx.x & (kWave - 1);
   const int Hq = p.num_q_heads;
   const int64_t nw = int64_t(gridDim.x) * (blockDim.x / kWave);
@@ -850,19 +870,27 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeParams p) {
   for (int64_t w = int64_t(blockIdx.x) * (blockDim.x / kWave) + threadIdx.x / kWave; w < tasks; w += nw) {
     const int b = p.ws.merge_list[w / Hq], hq = int(w % Hq);
     const int n = p.ws.item_count[b];
-    const int64_t base = int64_t(p.ws.item_base[b]) * Hq + hq;
+    const float* base = p.ws.partials + (int64_t(p.ws.item_base[b]) * Hq + hq) * (D + 2);
+    const int64_t stride = int64_t(Hq) * (D + 2);
     float M = -INFINITY, l = 0.f, o[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) o[e] = 0.f;
-    for (int i0 = 0; i0 < n; i0 += kWave) {
-      const int cnt = n - i0 < kWave ? n - i0 : kWave;
+    for (int i0 = 0; i0 < n; i0 += K) {
+      const int cnt = n - i0 < K ? n - i0 : K;
       float mi = -INFINITY, li = 0.f;
       if (lane < cnt) {
-        const float* part = p.ws.partials + (base + int64_t(i0 + lane) * Hq) * (D + 2);
-        mi = part[D];
-        li = part[D + 1];
-        if (!(li > 0.f)) mi = -INFINITY;  // an item without context rows
+        const float* pm = base + (i0 + lane) * stride;
+        mi = pm[D];
+        li = pm[D + 1];
       }
+      float v[K][E];
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        const float* pk = base + (i0 + (k < cnt ? k : 0)) * stride + lane * E;
+#pragma unroll
+        for (int e = 0; e < E; ++e) v[k][e] = pk[e];
+      }
+      if (!(li > 0.f)) mi = -INFINITY;  // an item without context rows
       const float mc = wave_max<kWave>(mi);
       const float Mn = fmaxf(M, mc);
       if (Mn == -INFINITY) continue;
@@ -871,20 +899,11 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeParams p) {
       l = l * sc + wave_sum<kWave>(wi * li);
 #pragma unroll
       for (int e = 0; e < E; ++e) o[e] *= sc;
-      for (int i = 0; i < cnt; i += 4) {  // four independent loads in flight
-        float v[4][E], a[4];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          a[k] = __shfl(wi, i + k < cnt ? i + k : 0, kWave);
-          const float* part = p.ws.partials + (base + int64_t(i0 + (i + k < cnt ? i + k : i)) * Hq) * (D + 2);
+      for (int k = 0; k < K; ++k) {
+        const float a = __shfl(wi, k, kWave);  // 0 for k >= cnt
 #pragma unroll
-          for (int e = 0; e < E; ++e) v[k][e] = part[lane * E + e];
-        }
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-          if (i + k < cnt)
-#pragma unroll
-            for (int e = 0; e < E; ++e) o[e] = fmaf(a[k], v[k][e], o[e]);
+        for (int e = 0; e < E; ++e) o[e] = fmaf(a, v[k][e], o[e]);
       }
       M = Mn;
     }
