@@ -81,7 +81,7 @@ def lib():
         L.orc_probs.argtypes = [ctypes.c_int, ctypes.c_int, P, P, ctypes.c_double, P]
         L.orc_probs.restype = None
         L.orc_decode.argtypes = [ctypes.c_int, P, P, i64, P, i32, P, i32, P, P, i32, P,
-                                 ctypes.c_double, P, i32, P, P, P, i32]
+                                 ctypes.c_double, P, i32, P, P, P, i32, i32]
         L.orc_decode.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -205,8 +205,9 @@ def probs(q: np.ndarray, K: np.ndarray, sm_scale=1.0) -> np.ndarray:
 
 
 def decode(cache: HostCache, page_table, seq_lens, slot_ids, q_bf16, sm_scale=1.0,
-           subset=None, nthreads=0):
-    """Returns (out[n][Hq][D] fp64, lse[n][Hq] fp64, max merge gap)."""
+           subset=None, nthreads=0, q_int8=False):
+    """Returns (out[n][Hq][D] fp64, lse[n][Hq] fp64, max merge gap).  q_int8:
+    the integer-query variant (q quantized per query head, INT8 row rule)."""
     lay = cache.lay
     pt = np.ascontiguousarray(page_table, dtype=np.int32)
     sl = np.ascontiguousarray(seq_lens, dtype=np.int32)
@@ -221,7 +222,7 @@ def decode(cache: HostCache, page_table, seq_lens, slot_ids, q_bf16, sm_scale=1.
                           _ptr(cache.side), cache.num_slots, _ptr(pt), pt.shape[1], _ptr(sl),
                           _ptr(si), sl.size, _ptr(q), float(sm_scale), _ptr(sub),
                           0 if sub is None else sub.size, _ptr(out), _ptr(lse), _ptr(gap),
-                          int(nthreads))
+                          int(nthreads), 1 if q_int8 else 0)
     if rc != 0:
         raise ValueError(f"oracle decode rejected its input (code {rc})")
     return out, lse, float(gap[0])

@@ -108,14 +108,19 @@ void orc_probs(int n, int D, const double* q, const double* K, double sm_scale,
 
 /* ---- decode -------------------------------------------------------------- */
 /* For every sequence in subset (or all when subset == NULL) and every query
- * head: out[i][Hq][D], lse[i][Hq]; *max_gap = largest merge gap seen. */
+ * head: out[i][Hq][D], lse[i][Hq]; *max_gap = largest merge gap seen.
+ * q_int8 != 0 selects the integer-query variant of the "integer attention
+ * path" ([NEWS] Interpretation para 3): each query head's row of q is first
+ * quantized by the same symmetric rule as an INT8 cache row (orc_quant_sym,
+ * qmax 127, fp16 scale) and attention uses code x scale in place of q.  The
+ * pages do not say how the query enters the integer path; this is a reading. */
 int orc_decode(int fmt, const orc_layout* L, const uint8_t* pages,
                int64_t num_pages, const uint8_t* side, int32_t num_slots,
                const int32_t* page_table, int32_t max_pages,
                const int32_t* seq_lens, const int32_t* slot_ids, int32_t batch,
                const uint16_t* q, double sm_scale, const int32_t* subset,
                int32_t n_subset, double* out, double* lse, double* max_gap,
-               int32_t nthreads);
+               int32_t nthreads, int32_t q_int8);
 
 #ifdef __cplusplus
 }

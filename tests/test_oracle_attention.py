@@ -209,3 +209,44 @@ def test_empty_sequence_decodes_to_zero(orc):
     out, lse, _ = orc.decode(cache, alloc.page_table, lengths, None, q)
     assert np.all(out[0] == 0) and np.all(np.isneginf(lse[0]))
     assert np.all(np.isfinite(lse[1]))
+
+
+def test_int8_query_exact_grid_equals_plain(orc):
+    """A query already on the INT8 grid (integers times a power of two, largest
+    |integer| 127) is reproduced exactly by the integer-query quantizer, so the
+    integer-query decode equals the plain decode bit for bit."""
+    cfg = get_config(0)
+    lengths = np.array([300, 517], dtype=np.int32)
+    cache, alloc, q = build_host_cache(orc, cfg, orc.FMT_KV4, lengths)
+    rng = np.random.default_rng(9)
+    ints = rng.integers(-127, 128, size=q.shape).astype(np.float32)
+    ints[..., 0] = 127.0                                       # amax = 127 * 2^e in every row
+    qx = bf16_bits_from_f32(ints * np.float32(2.0 ** -9))
+    a = orc.decode(cache, alloc.page_table, lengths, None, qx)
+    b = orc.decode(cache, alloc.page_table, lengths, None, qx, q_int8=True)
+    np.testing.assert_array_equal(a[0], b[0])
+    np.testing.assert_array_equal(a[1], b[1])
+
+
+def test_int8_query_is_quantize_then_attend(orc):
+    """The integer-query decode of head hq equals attention (oracle attend over
+    the gathered rows) with that head's q replaced by its INT8 row codes x
+    scale from the pinned quantizer -- checks which row is quantized for which
+    head and sequence."""
+    cfg = get_config(0)
+    lengths = np.array([37, 300], dtype=np.int32)
+    cache, alloc, q = build_host_cache(orc, cfg, orc.FMT_KV4, lengths)
+    out, lse, _ = orc.decode(cache, alloc.page_table, lengths, None, q, q_int8=True)
+    plain, _, _ = orc.decode(cache, alloc.page_table, lengths, None, q)
+    assert np.abs(out - plain).max() > 0                       # the quantization does change q
+    g = cfg.g
+    for b in range(lengths.size):
+        for h in range(cfg.num_kv_heads):
+            K, V, reg = orc.gather(cache, alloc.page_table, lengths, None, b, h)
+            for j in range(g):
+                hq = h * g + j
+                codes, sbits = orc.quant_sym(q[b, hq], 127)
+                qv = codes.astype(np.float64) * orc.f16_to_f64(int(sbits))
+                o, l, _ = orc.attend(qv, K, V, reg)
+                np.testing.assert_array_equal(out[b, hq], o)
+                assert lse[b, hq] == l
