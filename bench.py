@@ -325,7 +325,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--variants", action="store_true", help="also time kv8 / bf16 / plain INT4")
+    ap.add_argument("--variants", action="store_true",
+                    help="also time kv8 / bf16 / plain INT4 / KV4 with the integer query")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--config", type=int, default=CFG_IDX, choices=(2, 3),
                     help="2: one Qwen3-8B-shaped layer, B=1024 (the default line); 3: the 36-layer "
@@ -389,9 +390,10 @@ def main():
     }
     if args.variants:
         var = {}
-        for fmt, name, S, R in ((kv4.FMT_KV8, "kv8", 0, 0), (kv4.FMT_BF16, "bf16", 0, 0),
-                                (kv4.FMT_KV4, "int4_plain", 0, 0)):
-            w2 = build_config(CFG_IDX, fmt, n_sink=S, n_recent=R)
+        for fmt, name, S, R, q8 in ((kv4.FMT_KV8, "kv8", 0, 0, False), (kv4.FMT_BF16, "bf16", 0, 0, False),
+                                    (kv4.FMT_KV4, "int4_plain", 0, 0, False),
+                                    (kv4.FMT_KV4, "kv4_rl_int8_query", None, None, True)):
+            w2 = build_config(CFG_IDX, fmt, n_sink=S, n_recent=R, int8_query=q8)
             w2.step_append()
             _, p2 = time_steps(w2, max(10, args.steps // 2), 3, append=False)
             b2 = algorithmic_bytes(w2, fmt)

@@ -82,12 +82,13 @@ class GpuWorkload:
         return self.q.view(torch.int16).cpu().numpy().view(np.uint16)
 
 
-def _layout(cfg, fmt, n_sink=None, n_recent=None):
+def _layout(cfg, fmt, n_sink=None, n_recent=None, int8_query=False):
     S = cfg.n_sink if n_sink is None else n_sink
     R = cfg.n_recent if n_recent is None else n_recent
     if fmt != kv4.FMT_KV4:
         S, R = 0, 0
-    return kv4.make_layout(cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim, S, R)
+        int8_query = False
+    return kv4.make_layout(cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim, S, R, int8_query=int8_query)
 
 
 def _i32(a, device):
@@ -111,7 +112,7 @@ def _outputs(cfg, layout, B, max_pages, device):
     return out, lse, ws
 
 
-def build_from_host(cfg_idx, fmt, lengths=None, n_sink=None, n_recent=None, device="cuda",
+def build_from_host(cfg_idx, fmt, lengths=None, n_sink=None, n_recent=None, device="cuda", int8_query=False,
                     token_by_token=False, slot_perm_seed=None, extra_pages=0, max_pages=None):
     """Small workloads: host draws per sequence, appended through the library."""
     import torch
@@ -119,7 +120,7 @@ def build_from_host(cfg_idx, fmt, lengths=None, n_sink=None, n_recent=None, devi
     cfg = get_config(cfg_idx)
     lengths = np.asarray(context_lengths(cfg) if lengths is None else lengths, dtype=np.int32)
     B = lengths.size
-    layout = _layout(cfg, fmt, n_sink, n_recent)
+    layout = _layout(cfg, fmt, n_sink, n_recent, int8_query)
     alloc = PageAllocator(lengths, seed=cfg.seed, extra_pages=extra_pages, max_pages=max_pages)
     cache = kv4.alloc_cache(fmt, layout, alloc.num_pages, B, device)
     hk, hv, hq = [], [], []
@@ -159,7 +160,7 @@ def build_from_host(cfg_idx, fmt, lengths=None, n_sink=None, n_recent=None, devi
     return wl
 
 
-def build_config(cfg_idx, fmt, layer=0, n_sink=None, n_recent=None, device="cuda",
+def build_config(cfg_idx, fmt, layer=0, n_sink=None, n_recent=None, device="cuda", int8_query=False,
                  keep_inputs=False, lengths=None):
     """Benchmark workloads: device draws; the last token of each sequence is
     left for the timed step (step_append)."""
@@ -168,7 +169,7 @@ def build_config(cfg_idx, fmt, layer=0, n_sink=None, n_recent=None, device="cuda
     cfg = get_config(cfg_idx)
     lengths = np.asarray(context_lengths(cfg) if lengths is None else lengths, dtype=np.int32)
     B = lengths.size
-    layout = _layout(cfg, fmt, n_sink, n_recent)
+    layout = _layout(cfg, fmt, n_sink, n_recent, int8_query)
     shared = cfg.group > 1
     alloc = PageAllocator(lengths, prompt_len=cfg.prompt_len if shared else 0,
                           group=cfg.group, seed=cfg.seed)
@@ -332,6 +333,7 @@ class MultiLayerWorkload:
 
 
 def build_layers(cfg_idx, fmt, n_layers=None, device="cuda", chunk_seqs=32, n_sink=None, n_recent=None,
+                 int8_query=False,
                  progress=None):
     """Many-layer workload: every layer's cache is built with device draws,
     chunk by chunk of sequences (so the bf16 draws of a whole layer are never
@@ -342,7 +344,7 @@ def build_layers(cfg_idx, fmt, n_layers=None, device="cuda", chunk_seqs=32, n_si
     L = int(cfg.layers if n_layers is None else n_layers)
     lengths = np.asarray(context_lengths(cfg), dtype=np.int32)
     B = lengths.size
-    layout = _layout(cfg, fmt, n_sink, n_recent)
+    layout = _layout(cfg, fmt, n_sink, n_recent, int8_query)
     alloc = PageAllocator(lengths, seed=cfg.seed)
     pt = _i32(alloc.page_table, device)
     sl = _i32(lengths, device)

@@ -72,10 +72,20 @@ typedef enum {
  * n_sink + n_recent <= 144 (the bound on the protected set, [NEWS]
  * Interpretation para 3).  n_sink = n_recent = 0 is plain INT4 KV.  The kv8_
  * and kvbf16_ entry points ignore n_sink / n_recent.
- * flags: 0, or KV4_LAYOUT_WIDE_PROTECTION, which lifts the bound to
- * n_sink + n_recent <= 4096 -- for studies of wider protection than the
- * method's; the kernels are the same.  Other bits: KV4_ERR_INVALID_ARG. */
+ * flags (bit mask; other bits: KV4_ERR_INVALID_ARG):
+ *   KV4_LAYOUT_WIDE_PROTECTION lifts the bound to n_sink + n_recent <= 4096,
+ *     for studies of wider protection than the method's; same kernels.
+ *   KV4_LAYOUT_INT8_QUERY makes kv4_decode_attention / kv4_decode_phases use
+ *     the integer query-key path of the "integer attention path" ([NEWS]
+ *     Interpretation para 3): each query head's row of q is quantized by the
+ *     INT8 row rule (symmetric, fp16 scale from the head's largest |q|,
+ *     qmax 127) and multiplied with the INT4 / INT8 key codes in exact integer
+ *     arithmetic; probabilities and values are as without the flag.  The
+ *     pages do not say how the query enters the integer path: a reading.
+ *     kv8_ / kvbf16_ decodes return KV4_ERR_UNSUPPORTED with it; appends
+ *     ignore it. */
 #define KV4_LAYOUT_WIDE_PROTECTION 1u
+#define KV4_LAYOUT_INT8_QUERY 2u
 #define KV4_WIDE_PROTECTION_MAX 4096
 typedef struct {
   int32_t num_q_heads;

@@ -38,6 +38,7 @@ class Layout(ctypes.Structure):
 
 
 LAYOUT_WIDE_PROTECTION = 1  # lifts the n_sink + n_recent <= 144 bound to 4096
+LAYOUT_INT8_QUERY = 2       # integer query-key products (kv4 decode only)
 
 
 class CacheDesc(ctypes.Structure):
@@ -121,10 +122,13 @@ def _stream(stream=None) -> int:
 
 
 def make_layout(num_q_heads, num_kv_heads, head_dim, n_sink, n_recent, page_size=16,
-                group_size=32, flags=None) -> Layout:
-    """flags None: KV4_LAYOUT_WIDE_PROTECTION exactly when n_sink + n_recent > 144."""
+                group_size=32, flags=None, int8_query=False) -> Layout:
+    """flags None: KV4_LAYOUT_WIDE_PROTECTION exactly when n_sink + n_recent > 144,
+    plus KV4_LAYOUT_INT8_QUERY when int8_query."""
     if flags is None:
         flags = LAYOUT_WIDE_PROTECTION if n_sink + n_recent > 144 else 0
+        if int8_query:
+            flags |= LAYOUT_INT8_QUERY
     return Layout(num_q_heads, num_kv_heads, head_dim, page_size, group_size, n_sink, n_recent, flags)
 
 

@@ -25,7 +25,7 @@ kv4_status layout_check(const kv4_layout* L, int fmt) {
   if (L->page_size != 16 || L->group_size != 32) return KV4_ERR_UNSUPPORTED;
   const int g = L->num_q_heads / L->num_kv_heads;
   if (g != 1 && g != 2 && g != 4 && g != 8) return KV4_ERR_UNSUPPORTED;
-  if (L->flags & ~KV4_LAYOUT_WIDE_PROTECTION) return KV4_ERR_INVALID_ARG;
+  if (L->flags & ~(KV4_LAYOUT_WIDE_PROTECTION | KV4_LAYOUT_INT8_QUERY)) return KV4_ERR_INVALID_ARG;
   const int max_prot = (L->flags & KV4_LAYOUT_WIDE_PROTECTION) ? KV4_WIDE_PROTECTION_MAX : kv4::kMaxProtected;
   if (fmt == kFmtKV4 && int64_t(L->n_sink) + L->n_recent > max_prot) return KV4_ERR_INVALID_ARG;
   return KV4_OK;
@@ -142,7 +142,12 @@ kv4_status decode_impl(int fmt, const kv4_layout* L, const kv4_cache* c, const k
     p.side = nullptr;
     p.num_slots = 0;
   }
-  return kv4::launch_decode(fmt, p, L->head_dim, phases, stream) == hipSuccess ? KV4_OK : KV4_ERR_LAUNCH;
+  int kfmt = fmt;
+  if (L->flags & KV4_LAYOUT_INT8_QUERY) {
+    if (fmt != kFmtKV4) return KV4_ERR_UNSUPPORTED;
+    kfmt = kv4::kFmtKV4Q8;
+  }
+  return kv4::launch_decode(kfmt, p, L->head_dim, phases, stream) == hipSuccess ? KV4_OK : KV4_ERR_LAUNCH;
 }
 
 constexpr unsigned kAllPhases = KV4_PHASE_PLAN | KV4_PHASE_ATTEND | KV4_PHASE_MERGE;

@@ -34,19 +34,10 @@ __device__ inline int find_seq(const int32_t* __restrict__ cu, int batch, int t,
 
 template <int E>
 __device__ inline void quantize(const float (&x)[E], float amax, float qmax, int (&code)[E], uint16_t& sbits) {
-  float s32 = amax / qmax;
-  s32 = fminf(s32, 65504.0f);
-  sbits = f32_to_f16_bits(s32);
-  float s16 = f16_to_f32(sbits);
+  sbits = quant_scale_bits(amax, qmax);
+  const float s16 = f16_to_f32(sbits);
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    float c = 0.0f;
-    if (s16 != 0.0f) {
-      c = rintf(x[e] / s16);
-      c = fminf(fmaxf(c, -qmax), qmax);
-    }
-    code[e] = int(c);
-  }
+  for (int e = 0; e < E; ++e) code[e] = quant_code(x[e], s16, qmax);
 }
 
 template <int E>

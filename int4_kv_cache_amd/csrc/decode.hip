@@ -64,6 +64,14 @@ __device__ inline bf16x8_t bf8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
 __device__ inline f32x4_t mfma(bf16x8_t a, bf16x8_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
+typedef int i32x4_t __attribute__((__vector_size__(16)));
+// int8 x int8 -> int32, 16 x 16 x 64: A lane L byte e = (row L%16, k 16(L/16)+e),
+// B lane L byte e = (k 16(L/16)+e, column L%16), D as for the bf16 MFMA.
+__device__ inline i32x4_t mfma_i8(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3, const uint32_t (&b)[4],
+                                  i32x4_t c) {
+  const i32x4_t va = {int(a0), int(a1), int(a2), int(a3)}, vb = {int(b[0]), int(b[1]), int(b[2]), int(b[3])};
+  return __builtin_amdgcn_mfma_i32_16x16x64_i8(va, vb, c, 0, 0, 0);
+}
 // two fp32 -> packed bf16 pair, round to nearest even
 __device__ inline uint32_t pack_bf16(float lo, float hi) {
   typedef __bf16 bf16x2_t __attribute__((__vector_size__(4)));
@@ -217,6 +225,8 @@ struct Unit {
   static constexpr int NT = D / 16;  // PV N-tiles
   bf16x8_t bq[NG];                   // q operand per QK MFMA
   float qsum;                        // sum of this lane's row (head, group) of q
+  uint32_t q8[(D / 64) > 0 ? D / 64 : 1][4];  // integer query: INT8 codes per i8 MFMA
+  int cin8;                          // integer query: -8 x the row group's code sum
   f32x4_t o[NT];                     // PV accumulators (D layout)
   f32x4_t corr;                      // INT4 V-encoding correction per row (D layout)
   float m;                           // running max (log2 units) of head ln / NG
@@ -226,11 +236,37 @@ struct Unit {
 
 // QK for one tile -> x[e] = per-group partial score of position 4kg+e, before
 // the softmax scale (and, for INT4, before the factor 16 of the encoding).
-template <int KIND, int D>
+template <int KIND, int D, bool Q8>
 __device__ inline void qk_tile(const Unit<D>& u, const Tile<KIND, D>& T, float (&x)[4]) {
   constexpr int NG = D / 32;
   f32x4_t acc;
-  if constexpr (KIND == kInt4Page) {
+  if constexpr (Q8 && KIND != kBf16Page) {
+    // Integer query: i8 MFMAs over 64 channels (16 per lane, taken in the
+    // order even channels then odd channels of each 8-channel half, which is
+    // how the nibbles unpack; the query codes are stored in the same order).
+    constexpr int MQ = D / 64;
+    i32x4_t ai;
+    if constexpr (KIND == kInt4Page) {
+      // nibble -> byte (code + 8); the offset is removed through cin8
+      ai = i32x4_t{u.cin8, u.cin8, u.cin8, u.cin8};
+#pragma unroll
+      for (int t = 0; t < MQ; ++t) {
+        const uint32_t d0 = T.k[2 * t], d1 = T.k[2 * t + 1];
+        ai = mfma_i8((d0 & 0x0F0F0F0Fu) ^ 0x08080808u, ((d0 >> 4) & 0x0F0F0F0Fu) ^ 0x08080808u,
+                     (d1 & 0x0F0F0F0Fu) ^ 0x08080808u, ((d1 >> 4) & 0x0F0F0F0Fu) ^ 0x08080808u, u.q8[t], ai);
+      }
+    } else {
+      ai = i32x4_t{0, 0, 0, 0};
+#pragma unroll
+      for (int t = 0; t < MQ; ++t) {
+        const uint32_t w0 = T.k[4 * t], w1 = T.k[4 * t + 1], w2 = T.k[4 * t + 2], w3 = T.k[4 * t + 3];
+        ai = mfma_i8(__builtin_amdgcn_perm(w1, w0, 0x06040200u), __builtin_amdgcn_perm(w1, w0, 0x07050301u),
+                     __builtin_amdgcn_perm(w3, w2, 0x06040200u), __builtin_amdgcn_perm(w3, w2, 0x07050301u), u.q8[t],
+                     ai);
+      }
+    }
+    acc = f32x4_t{float(ai[0]), float(ai[1]), float(ai[2]), float(ai[3])};
+  } else if constexpr (KIND == kInt4Page) {
     const float c = -1.5f * u.qsum;
     acc = f32x4_t{c, c, c, c};
 #pragma unroll
@@ -299,7 +335,7 @@ __device__ inline float head_value_for_acc(float v, int lane, int e) {
 }
 
 // One step: two 16-row tiles (32 positions).  mask0/mask1: 16-bit row masks.
-template <int KIND, int D, bool MASKED>
+template <int KIND, int D, bool MASKED, bool Q8>
 __device__ inline void step(Unit<D>& u, const Tile<KIND, D>& T0, const Tile<KIND, D>& T1, uint32_t mask0,
                             uint32_t mask1, int lane) {
   constexpr int NG = D / 32;
@@ -308,8 +344,8 @@ __device__ inline void step(Unit<D>& u, const Tile<KIND, D>& T0, const Tile<KIND
   const uint32_t va0 = (mask0 >> (4 * kg)) & 15u, va1 = (mask1 >> (4 * kg)) & 15u;
 
   float x0[4], x1[4];
-  qk_tile<KIND, D>(u, T0, x0);
-  qk_tile<KIND, D>(u, T1, x1);
+  qk_tile<KIND, D, Q8>(u, T0, x0);
+  qk_tile<KIND, D, Q8>(u, T1, x1);
   // sum the per-group partial scores of a head (lanes 4h..4h+3 or 2h..2h+1)
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
@@ -329,7 +365,7 @@ __device__ inline void step(Unit<D>& u, const Tile<KIND, D>& T0, const Tile<KIND
   }
   float mx = max3(max3(x0[0], x0[1], x0[2]), max3(x0[3], x1[0], x1[1]), max3(x1[2], x1[3], -INFINITY));
   // score (log2 units) = sc * x; INT4 partials carry the encoding's 1/16
-  const float sc = KIND == kInt4Page ? 16.0f * u.qk_scale : u.qk_scale;
+  const float sc = (KIND == kInt4Page && !Q8) ? 16.0f * u.qk_scale : u.qk_scale;
 
   // The running max of a head is only re-referenced when a score exceeds it
   // by 2^kRescale (then to the head's exact maximum so far), so p <= 2^8 and
@@ -415,7 +451,7 @@ __device__ inline void step(Unit<D>& u, const Tile<KIND, D>& T0, const Tile<KIND
 // (past the end it re-reads the last step, which the L2 holds) so the loop
 // body has one fixed load sequence and each wait covers exactly the step it
 // needs.  Tile n (odd n) is a masked copy of tile n-1.
-template <int KIND, int D, int STAGES, class PtrFn, class MaskFn, class SetupFn>
+template <int KIND, int D, int STAGES, bool Q8, class PtrFn, class MaskFn, class SetupFn>
 __device__ inline void run_tiles(Unit<D>& u, int n, PtrFn ptr, MaskFn mask, int lane, SetupFn setup) {
   if (n <= 0) return;
   const LaneOff<KIND, D> off(lane & 15, lane >> 4);
@@ -429,7 +465,7 @@ __device__ inline void run_tiles(Unit<D>& u, int n, PtrFn ptr, MaskFn mask, int 
   };
   auto run = [&](const Tile<KIND, D>& t0, const Tile<KIND, D>& t1, int s) {
     const int i = 2 * s;
-    step<KIND, D, true>(u, t0, t1, mask(i), i + 1 < n ? mask(i + 1) : 0u, lane);
+    step<KIND, D, true, Q8>(u, t0, t1, mask(i), i + 1 < n ? mask(i + 1) : 0u, lane);
   };
   if constexpr (STAGES == 1) {
     for (int s = 0; s < nsteps; ++s) {
@@ -683,14 +719,16 @@ template <int FMT, int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KV4_WAVES_PER_EU, 8))) void attention_kernel(
     DecodeParams p) {
   constexpr int NG = D / 32, HB = 16 / NG, NT = D / 16;
-  constexpr int MAIN = FMT == kFmtKV4 ? kInt4Page : (FMT == kFmtKV8 ? kInt8Tile : kBf16Page);
+  constexpr bool KV4 = FMT == kFmtKV4 || FMT == kFmtKV4Q8;
+  constexpr bool Q8 = FMT == kFmtKV4Q8;
+  constexpr int MAIN = KV4 ? kInt4Page : (FMT == kFmtKV8 ? kInt8Tile : kBf16Page);
   const int lane = threadIdx.x & (kWave - 1);
   const int ln = lane & 15, kg = lane >> 4;
   const int H = p.num_kv_heads, Hq = p.num_q_heads, G = Hq / H;
   const int NHB = (G + HB - 1) / HB;
   const int UPI = H * NHB;  // units per item
-  const int S = FMT == kFmtKV4 ? p.n_sink : 0;
-  const int R = FMT == kFmtKV4 ? p.n_recent : 0;
+  const int S = KV4 ? p.n_sink : 0;
+  const int R = KV4 ? p.n_recent : 0;
   // unit indices fit 32 bits: the host bounds the work list (items x units per item < 2^31)
   const uint32_t units = p.ws.header[1] * uint32_t(UPI);
   if (units == 0) return;
@@ -757,6 +795,55 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KV4_WAVES_P
     auto setup = [&]() {
       if (!pending) return;
       pending = false;
+      if constexpr (Q8) {
+        // Integer query: the head's row of q is quantized by the INT8 row rule
+        // (scale from the head's largest |q|).  The lanes holding a row's
+        // group quantize it; the head maximum gathers the head's rows.
+        float am = 0.f;
+#pragma unroll
+        for (int t = 0; t < NG; ++t) {
+          const uint32_t w[4] = {qraw[t].x, qraw[t].y, qraw[t].z, qraw[t].w};
+#pragma unroll
+          for (int k = 0; k < 4; ++k) am = max3(am, fabsf(bf16_lo(w[k])), fabsf(bf16_hi(w[k])));
+        }
+        am = fmaxf(am, __shfl_xor(am, 16, kWave));
+        am = fmaxf(am, __shfl_xor(am, 32, kWave));
+        am = fmaxf(am, quad_xor1(am));
+        if constexpr (NG == 4) am = fmaxf(am, quad_xor2(am));
+        const float qs16 = f16_to_f32(quant_scale_bits(am, 127.0f));
+        int isum = 0;
+#pragma unroll
+        for (int t = 0; t < D / 64; ++t) {
+          // 16 channels: qraw[2t] holds 0..7, qraw[2t+1] holds 8..15; bytes in
+          // the order 0 2 4 6 | 1 3 5 7 | 8 10 12 14 | 9 11 13 15
+          const uint32_t a[4] = {qraw[2 * t].x, qraw[2 * t].y, qraw[2 * t].z, qraw[2 * t].w};
+          const uint32_t c[4] = {qraw[2 * t + 1].x, qraw[2 * t + 1].y, qraw[2 * t + 1].z, qraw[2 * t + 1].w};
+          int ev[8], od[8];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            ev[k] = quant_code(bf16_lo(a[k]), qs16, 127.0f);
+            od[k] = quant_code(bf16_hi(a[k]), qs16, 127.0f);
+            ev[4 + k] = quant_code(bf16_lo(c[k]), qs16, 127.0f);
+            od[4 + k] = quant_code(bf16_hi(c[k]), qs16, 127.0f);
+          }
+          auto pack = [](const int* v) {
+            return (uint32_t(v[0]) & 0xFFu) | ((uint32_t(v[1]) & 0xFFu) << 8) | ((uint32_t(v[2]) & 0xFFu) << 16) |
+                   ((uint32_t(v[3]) & 0xFFu) << 24);
+          };
+          u.q8[t][0] = pack(ev);
+          u.q8[t][1] = pack(od);
+          u.q8[t][2] = pack(ev + 4);
+          u.q8[t][3] = pack(od + 4);
+#pragma unroll
+          for (int k = 0; k < 8; ++k) isum += ev[k] + od[k];
+        }
+        // the row group's code sum: the other lanes of the row hold zeros
+        isum += __shfl_xor(isum, 16, kWave);
+        isum += __shfl_xor(isum, 32, kWave);
+        u.cin8 = -8 * isum;
+        u.qk_scale = p.softmax_scale * kLog2e * qs16;
+        return;
+      }
       float qs = 0.f;
 #pragma unroll
       for (int t = 0; t < NG; ++t) {
@@ -778,7 +865,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KV4_WAVES_P
     };
 
     // ---- protected rows: INT8 side-cache tiles (sinks, then the ring)
-    if (FMT == kFmtKV4 && d.ck == 0 && L > 0 && S + R > 0 && d.slot >= 0 && d.slot < p.num_slots) {
+    if (KV4 && d.ck == 0 && L > 0 && S + R > 0 && d.slot >= 0 && d.slot < p.num_slots) {
       const int se = L < S ? L : S;
       const int nring = L > S ? (L - S < R ? L - S : R) : 0;
       const int rows = nring > 0 ? S + nring : se;
@@ -789,7 +876,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KV4_WAVES_P
         const int r0 = i * kPage;
         return range_mask(0 - r0, se - r0) | range_mask(S - r0, S + nring - r0);
       };
-      run_tiles<kInt8Tile, D, KV4_STAGES8>(u, ntiles, ptr, mask, lane, setup);
+      run_tiles<kInt8Tile, D, KV4_STAGES8, Q8>(u, ntiles, ptr, mask, lane, setup);
     }
 
     // ---- middle pages of this item (at most 64: one page id per lane)
@@ -803,7 +890,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KV4_WAVES_P
         const int p0 = (d.first + i) * kPage;
         return pid < 0 ? 0u : range_mask(g.mb - p0, g.me - p0);
       };
-      run_tiles<MAIN, D, MAIN == kInt4Page ? KV4_STAGES : (MAIN == kInt8Tile ? KV4_STAGES8 : 1)>(u, d.npg, ptr,
+      run_tiles<MAIN, D, MAIN == kInt4Page ? KV4_STAGES : (MAIN == kInt8Tile ? KV4_STAGES8 : 1), Q8>(u, d.npg, ptr,
                                                                                                    mask, lane, setup);
     }
 
@@ -1016,6 +1103,7 @@ DecodeWorkspace carve_workspace(void* base, int32_t batch, int32_t max_pages, in
 
 hipError_t launch_decode(int fmt, const DecodeParams& p, int head_dim, unsigned phases, hipStream_t stream) {
   if (fmt == kFmtKV4) return launch_fmt<kFmtKV4>(p, head_dim, phases, stream);
+  if (fmt == kFmtKV4Q8) return launch_fmt<kFmtKV4Q8>(p, head_dim, phases, stream);
   if (fmt == kFmtKV8) return launch_fmt<kFmtKV8>(p, head_dim, phases, stream);
   return launch_fmt<kFmtBF16>(p, head_dim, phases, stream);
 }

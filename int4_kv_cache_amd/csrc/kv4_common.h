@@ -15,7 +15,9 @@ constexpr int kGroup = 32;  // channels per INT4 scale group
 constexpr int kWave = 64;
 constexpr int kMaxProtected = 144;  // sinks + recent, the pages' bound
 
-enum Format : int { kFmtKV4 = 0, kFmtKV8 = 1, kFmtBF16 = 2 };
+// kFmtKV4Q8: the KV4 cache read with an INT8-quantized query (the integer
+// query-key products of the "integer attention path" variant).
+enum Format : int { kFmtKV4 = 0, kFmtKV8 = 1, kFmtBF16 = 2, kFmtKV4Q8 = 3 };
 
 // ---- block sizes ------------------------------------------------------------
 __host__ __device__ constexpr size_t int4_block_bytes(int D) { return size_t(18) * D; }
@@ -78,6 +80,17 @@ __device__ inline float f16_to_f32(uint16_t h) { return float(__builtin_bit_cast
 // Round to nearest even (the hardware default rounding mode).
 __device__ inline uint16_t f32_to_f16_bits(float x) { return __builtin_bit_cast(uint16_t, _Float16(x)); }
 __device__ inline uint16_t f32_to_bf16_bits(float x) { return __builtin_bit_cast(uint16_t, __bf16(x)); }
+
+// ---- the symmetric quantizer (append and the integer query) -------------------
+// scale = fp16_rne(min(amax / qmax, 65504)), fp32 divide; returns its bits.
+__device__ inline uint16_t quant_scale_bits(float amax, float qmax) {
+  return f32_to_f16_bits(fminf(amax / qmax, 65504.0f));
+}
+// code = clamp(rint(x / scale), -qmax, qmax) (fp32 divide, ties to even); 0 if scale is 0.
+__device__ inline int quant_code(float x, float scale, float qmax) {
+  if (scale == 0.0f) return 0;
+  return int(fminf(fmaxf(rintf(x / scale), -qmax), qmax));
+}
 
 // ---- wave reductions ---------------------------------------------------------
 template <int WIDTH>

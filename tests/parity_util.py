@@ -132,8 +132,9 @@ def decode_metrics(wl, sample, ocache=None, pt=None, lens=None, nthreads=0):
     if ocache is None:
         ocache, pt, lens = oracle_cache_for(wl, sample)
     q = wl.host_q()[np.asarray(sample)]
+    q_int8 = bool(wl.layout.flags & 2)   # the integer-query layout flag
     out64, lse64, gap = oracle.decode(ocache, pt, lens, None, np.ascontiguousarray(q), 1.0,
-                                      nthreads=nthreads)
+                                      nthreads=nthreads, q_int8=q_int8)
     import torch
 
     og = bf16_bits_to_f64(wl.out.view(torch.int16).cpu().numpy()[np.asarray(sample)])

@@ -83,7 +83,7 @@ def test_host_argument_errors_return_before_launch(lib):
                       (kv4.make_layout(32, 8, 96, 16, 128), -2),     # head_dim
                       (kv4.make_layout(32, 8, 128, 16, 129, flags=0), -1),    # S + R > 144
                       (kv4.make_layout(32, 8, 128, 16, 4081), -1),   # > 4096 even when widened
-                      (kv4.make_layout(32, 8, 128, 16, 128, flags=2), -1),    # unknown flag
+                      (kv4.make_layout(32, 8, 128, 16, 128, flags=8), -1),    # unknown flag
                       (kv4.make_layout(32, 8, 128, -1, 0), -1),
                       (kv4.make_layout(32, 8, 128, 16, 128, page_size=32), -2),
                       (kv4.make_layout(32, 8, 128, 16, 128, group_size=64), -2),
@@ -105,6 +105,13 @@ def test_host_argument_errors_return_before_launch(lib):
     for sm in (0.0, -1.0, float("inf"), float("nan")):
         assert lib.kv4_decode_attention(ctypes.byref(good), ctypes.byref(cache), ctypes.byref(batch), fake,
                                         sm, fake, None, fake, 1 << 40, None) == -1
+    # the integer-query flag: kv4 only; unknown flag bits are rejected
+    q8 = kv4.make_layout(32, 8, 128, 16, 128, int8_query=True)
+    assert q8.flags == kv4.LAYOUT_INT8_QUERY
+    assert _call_decode(lib, q8, cache, batch, ws_bytes=16) == -3
+    assert lib.kv8_decode_attention(ctypes.byref(q8), ctypes.byref(cache), ctypes.byref(batch), fake, 1.0, fake,
+                                    None, fake, 1 << 40, None) == -2
+    assert _call_decode(lib, kv4.make_layout(32, 8, 128, 16, 128, flags=4), cache, batch) == -1
     # wider protection is accepted behind the flag (then the workspace check is reached)
     wide = kv4.make_layout(32, 8, 128, 32, 480)
     assert wide.flags == kv4.LAYOUT_WIDE_PROTECTION

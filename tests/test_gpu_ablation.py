@@ -1,6 +1,7 @@
 """Config 4, precision ablation at the config-2 shapes: BF16-KV, all-INT8-KV,
-plain INT4-KV (no protection) and KV4-RL (INT4 + 16 sink / 128 recent INT8
-rows) on identical seeded K/V.  Each variant's GPU output is compared with
+plain INT4-KV (no protection), KV4-RL (INT4 + 16 sink / 128 recent INT8
+rows) and KV4-RL with the integer query (INT8-quantized q) on identical
+seeded K/V.  Each variant's GPU output is compared with
 the GPU BF16 output (max-abs over every (sequence, query head)), and the
 attention distributions of a seeded sample of 128 sequences are compared
 with BF16's in the oracle (KL(pi_bf16 || pi_variant), fp64).
@@ -26,8 +27,8 @@ def _kl_stats(wls, sample):
     import oracle
 
     caches = {name: pu.oracle_cache_for(wl, sample) for name, wl in wls.items()}
-    q = wls["bf16"].host_q()[sample].astype(np.uint32) << 16
-    qf = q.view(np.float32).astype(np.float64)               # [n][Hq][D]
+    qbits = wls["bf16"].host_q()[sample]
+    qf = (qbits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)   # [n][Hq][D]
     lay = wls["bf16"].layout
     g = lay.num_q_heads // lay.num_kv_heads
     kl = {name: [] for name in wls if name != "bf16"}
@@ -40,7 +41,11 @@ def _kl_stats(wls, sample):
                 hq = h * g + j
                 p_ref = oracle.probs(qf[i, hq], Ks["bf16"])
                 for name in kl:
-                    p = oracle.probs(qf[i, hq], Ks[name])
+                    qv = qf[i, hq]
+                    if wls[name].layout.flags & 2:   # integer query: q -> INT8 row codes x scale
+                        codes, sbits = oracle.quant_sym(qbits[i, hq], 127)
+                        qv = codes.astype(np.float64) * oracle.f16_to_f64(int(sbits))
+                    p = oracle.probs(qv, Ks[name])
                     kl[name].append(float(np.sum(p_ref * (np.log(p_ref) - np.log(p)))))
     return {name: (float(np.mean(v)), float(np.max(v))) for name, v in kl.items()}
 
@@ -52,12 +57,13 @@ def test_config4_precision_ablation(kv4):
 
     gc.collect()
     torch.cuda.empty_cache()
-    variants = {"bf16": (kv4.FMT_BF16, None, None), "kv8": (kv4.FMT_KV8, None, None),
-                "int4_plain": (kv4.FMT_KV4, 0, 0), "kv4_rl": (kv4.FMT_KV4, None, None)}
+    variants = {"bf16": (kv4.FMT_BF16, None, None, False), "kv8": (kv4.FMT_KV8, None, None, False),
+                "int4_plain": (kv4.FMT_KV4, 0, 0, False), "kv4_rl": (kv4.FMT_KV4, None, None, False),
+                "kv4_rl_q8": (kv4.FMT_KV4, None, None, True)}
     wls = {}
     try:
-        for name, (fmt, S, R) in variants.items():
-            wl = build_config(4, fmt, n_sink=S, n_recent=R, keep_inputs=True)
+        for name, (fmt, S, R, q8) in variants.items():
+            wl = build_config(4, fmt, n_sink=S, n_recent=R, keep_inputs=True, int8_query=q8)
             wl.step_append()
             wl.decode()
             torch.cuda.synchronize()

@@ -154,3 +154,49 @@ def test_config2_full_size_bench_launch(kv4):
     sample = np.unique(np.concatenate([order[:6], order[-6:], rng.choice(1024, 20, replace=False),
                                        np.arange(8)]))   # a whole prompt group
     _check_all(wl, sample)
+
+
+# ---- the integer query-key path (KV4_LAYOUT_INT8_QUERY) ----------------------
+def test_int8_query_config0_and_edges(kv4):
+    from harness import build_from_host
+
+    wl = build_from_host(0, kv4.FMT_KV4, int8_query=True)
+    _run(kv4, wl)
+    _check_all(wl)
+    wl = build_from_host(0, kv4.FMT_KV4, lengths=EDGE_LENGTHS, slot_perm_seed=3, int8_query=True)
+    _run(kv4, wl)
+    _check_all(wl)
+    wl = build_from_host(0, kv4.FMT_KV4, n_sink=0, n_recent=0, int8_query=True)
+    _run(kv4, wl)
+    _check_all(wl)
+
+
+@pytest.mark.parametrize("hq,hkv,d", [(32, 8, 128), (8, 8, 128), (16, 8, 64), (8, 1, 64), (16, 2, 128)])
+def test_int8_query_head_shapes(kv4, hq, hkv, d):
+    import dataclasses
+
+    import workloads.configs as wc
+    from harness import build_from_host
+
+    base = wc.CONFIGS[0]
+    cfg = dataclasses.replace(base, idx=91, name=f"q8-shape-{hq}-{hkv}-{d}", num_q_heads=hq,
+                              num_kv_heads=hkv, head_dim=d, n_sink=16, n_recent=128, n_outlier=6)
+    wc.CONFIGS[91] = cfg
+    try:
+        wl = build_from_host(91, kv4.FMT_KV4, lengths=[1, 160, 1300, 77], int8_query=True)
+        _run(kv4, wl)
+        _check_all(wl)
+    finally:
+        del wc.CONFIGS[91]
+
+
+def test_int8_query_config2_full_size(kv4):
+    from harness import build_config
+
+    wl = build_config(2, kv4.FMT_KV4, keep_inputs=True, int8_query=True)
+    wl.step_append()
+    _run(kv4, wl)
+    order = np.argsort(wl.lengths)
+    rng = np.random.default_rng(1)
+    sample = np.unique(np.concatenate([order[:6], order[-6:], rng.choice(1024, 20, replace=False)]))
+    _check_all(wl, sample)
