@@ -153,6 +153,41 @@ struct LaneOff {
   }
 };
 
+// Tile reads go through a buffer resource whose range is the tile, so a load
+// issued for a step past the end of a run (the pipeline issues every load
+// unconditionally) gets an empty range and returns zeros without reading
+// memory.  INT4 pages that no other sequence of the batch shares are read
+// with the nontemporal hint: every load instruction covers whole 128-byte
+// lines and each byte is read once per decode step, and on gfx950 the hint
+// raises the sustained streaming read rate.  Shared prompt pages, INT8 and
+// bf16 tiles keep the default policy: the first are read again by the other
+// sequences of the group, the others are read in half-line pieces, and both
+// need their lines to stay in the caches in between.
+#ifndef KV4_NT_LOADS
+#define KV4_NT_LOADS 1  // 0: no hint anywhere
+#endif
+
+struct TileSrc {
+  __amdgpu_buffer_rsrc_t r;
+  __device__ inline TileSrc(const uint8_t* base, int bytes)
+      : r(__builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), short(0), bytes, 0x00020000)) {}
+};
+
+typedef uint32_t ldv4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t ldv2_t __attribute__((ext_vector_type(2)));
+
+template <bool NT>
+__device__ inline uint4 ld16(const TileSrc& t, uint32_t off) {
+  const ldv4_t r = __builtin_amdgcn_raw_buffer_load_b128(t.r, off, 0, NT ? 2 : 0);
+  return make_uint4(r.x, r.y, r.z, r.w);
+}
+
+template <bool NT>
+__device__ inline uint2 ld8(const TileSrc& t, uint32_t off) {
+  const ldv2_t r = __builtin_amdgcn_raw_buffer_load_b64(t.r, off, 0, NT ? 2 : 0);
+  return make_uint2(r.x, r.y);
+}
+
 template <int KIND, int D>
 struct Tile;
 
@@ -162,20 +197,22 @@ struct Tile<kInt4Page, D> {
   uint32_t k[KW];
   uint32_t v[KW];
   uint32_t ks[2], vs[2];  // fp16 scales of positions 4kg..4kg+3, group = ln % NG
-  __device__ inline void load(const uint8_t* __restrict__ blk, const LaneOff<kInt4Page, D>& o) {
+  static constexpr int kBytes = int(int4_block_bytes(D));
+  template <bool NT>
+  __device__ inline void load(const TileSrc& blk, const LaneOff<kInt4Page, D>& o) {
     if constexpr (KW == 4) {
-      const uint4 a = *reinterpret_cast<const uint4*>(blk + o.k);
-      const uint4 b = *reinterpret_cast<const uint4*>(blk + o.v);
+      const uint4 a = ld16<NT>(blk, o.k);
+      const uint4 b = ld16<NT>(blk, o.v);
       k[0] = a.x; k[1] = a.y; k[2] = a.z; k[3] = a.w;
       v[0] = b.x; v[1] = b.y; v[2] = b.z; v[3] = b.w;
     } else {
-      const uint2 a = *reinterpret_cast<const uint2*>(blk + o.k);
-      const uint2 b = *reinterpret_cast<const uint2*>(blk + o.v);
+      const uint2 a = ld8<NT>(blk, o.k);
+      const uint2 b = ld8<NT>(blk, o.v);
       k[0] = a.x; k[1] = a.y;
       v[0] = b.x; v[1] = b.y;
     }
-    const uint2 s = *reinterpret_cast<const uint2*>(blk + o.ks);
-    const uint2 t = *reinterpret_cast<const uint2*>(blk + o.vs);
+    const uint2 s = ld8<NT>(blk, o.ks);
+    const uint2 t = ld8<NT>(blk, o.vs);
     ks[0] = s.x; ks[1] = s.y;
     vs[0] = t.x; vs[1] = t.y;
   }
@@ -187,16 +224,18 @@ struct Tile<kInt8Tile, D> {
   uint32_t k[KW];
   uint32_t v[KW];
   uint32_t ks[2], vs[2];
-  __device__ inline void load(const uint8_t* __restrict__ tile, const LaneOff<kInt8Tile, D>& o) {
+  static constexpr int kBytes = int(int8_tile_bytes(D));
+  template <bool NT>
+  __device__ inline void load(const TileSrc& tile, const LaneOff<kInt8Tile, D>& o) {
 #pragma unroll
     for (int i = 0; i < KW / 4; ++i) {
-      const uint4 a = *reinterpret_cast<const uint4*>(tile + o.k + 16 * i);
-      const uint4 b = *reinterpret_cast<const uint4*>(tile + o.v + 16 * i);
+      const uint4 a = ld16<NT>(tile, o.k + 16 * i);
+      const uint4 b = ld16<NT>(tile, o.v + 16 * i);
       k[4 * i] = a.x; k[4 * i + 1] = a.y; k[4 * i + 2] = a.z; k[4 * i + 3] = a.w;
       v[4 * i] = b.x; v[4 * i + 1] = b.y; v[4 * i + 2] = b.z; v[4 * i + 3] = b.w;
     }
-    const uint2 s = *reinterpret_cast<const uint2*>(tile + o.ks);
-    const uint2 t = *reinterpret_cast<const uint2*>(tile + o.vs);
+    const uint2 s = ld8<NT>(tile, o.ks);
+    const uint2 t = ld8<NT>(tile, o.vs);
     ks[0] = s.x; ks[1] = s.y;
     vs[0] = t.x; vs[1] = t.y;
   }
@@ -207,11 +246,13 @@ struct Tile<kBf16Page, D> {
   static constexpr int KW = D / 8;  // D/2 bytes per lane
   uint32_t k[KW];
   uint32_t v[KW];
-  __device__ inline void load(const uint8_t* __restrict__ tile, const LaneOff<kBf16Page, D>& o) {
+  static constexpr int kBytes = int(bf16_tile_bytes(D));
+  template <bool NT>
+  __device__ inline void load(const TileSrc& tile, const LaneOff<kBf16Page, D>& o) {
 #pragma unroll
     for (int i = 0; i < KW / 4; ++i) {
-      const uint4 a = *reinterpret_cast<const uint4*>(tile + o.k + 16 * i);
-      const uint4 b = *reinterpret_cast<const uint4*>(tile + o.v + 16 * i);
+      const uint4 a = ld16<NT>(tile, o.k + 16 * i);
+      const uint4 b = ld16<NT>(tile, o.v + 16 * i);
       k[4 * i] = a.x; k[4 * i + 1] = a.y; k[4 * i + 2] = a.z; k[4 * i + 3] = a.w;
       v[4 * i] = b.x; v[4 * i + 1] = b.y; v[4 * i + 2] = b.z; v[4 * i + 3] = b.w;
     }
@@ -448,20 +489,24 @@ __device__ inline void step(Unit<D>& u, const Tile<KIND, D>& T0, const Tile<KIND
 // Runs n tiles (ptr(i), mask(i)) two at a time (a step).  STAGES = 1: load
 // then compute; 2: the next step's loads are in flight while a step is
 // computed; 3: the next two steps'.  Every load is issued unconditionally
-// (past the end it re-reads the last step, which the L2 holds) so the loop
-// body has one fixed load sequence and each wait covers exactly the step it
-// needs.  Tile n (odd n) is a masked copy of tile n-1.
-template <int KIND, int D, int STAGES, bool Q8, class PtrFn, class MaskFn, class SetupFn>
+// (past the end with an empty range) so the loop body has one fixed load
+// sequence and each wait covers exactly the step it needs.  Tile n (odd n)
+// reads as zeros and is masked.
+template <int KIND, int D, int STAGES, bool Q8, bool NT, class PtrFn, class MaskFn, class SetupFn>
 __device__ inline void run_tiles(Unit<D>& u, int n, PtrFn ptr, MaskFn mask, int lane, SetupFn setup) {
   if (n <= 0) return;
   const LaneOff<KIND, D> off(lane & 15, lane >> 4);
   const int nsteps = (n + 1) >> 1;
   const int last = nsteps - 1;
+  constexpr int kBytes = Tile<KIND, D>::kBytes;
+  // steps past the last and the tile after an odd last one get an empty
+  // range: their loads return zeros and read no memory
   auto load = [&](Tile<KIND, D>& t0, Tile<KIND, D>& t1, int s) {
+    const bool live = s <= last;
     s = s < last ? s : last;
     const int i = 2 * s;
-    t0.load(ptr(i), off);
-    t1.load(ptr(i + 1 < n ? i + 1 : i), off);
+    t0.template load<NT>(TileSrc(ptr(i), live ? kBytes : 0), off);
+    t1.template load<NT>(TileSrc(ptr(i + 1 < n ? i + 1 : i), live && i + 1 < n ? kBytes : 0), off);
   };
   auto run = [&](const Tile<KIND, D>& t0, const Tile<KIND, D>& t1, int s) {
     const int i = 2 * s;
@@ -741,24 +786,38 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KV4_WAVES_P
   // ids of unit k+1 are loaded when unit k starts.
   const uint32_t nw = gridDim.x * (blockDim.x / kWave);
   auto item_of = [&](uint32_t t) -> uint32_t { return (t < units ? t : units - 1) / uint32_t(UPI); };
-  auto fetch_pids = [&](const ItemDesc& d) -> int {
+  // Page ids of an item, one per lane, and the pages it shares with the
+  // sequence before or after it in the batch (the same physical page at the
+  // same index: a shared prompt), as a lane mask.
+  struct Pids {
+    int pid;
+    uint64_t shared;
+  };
+  auto fetch_pids = [&](const ItemDesc& d) -> Pids {
     int v = 0;
+    bool sh = false;
     if (lane < d.npg) {
-      const int64_t x = p.page_table[int64_t(d.b) * p.max_pages + d.first + lane];
+      const int64_t at = int64_t(d.b) * p.max_pages + d.first + lane;
+      const int64_t x = p.page_table[at];
       v = (x < 0 || x >= p.num_pages) ? -1 : int(x);
+      if constexpr (KV4 && KV4_NT_LOADS) {
+        const int xp = d.b > 0 ? p.page_table[at - p.max_pages] : -1;
+        const int xn = d.b + 1 < p.batch ? p.page_table[at + p.max_pages] : -1;
+        sh = v >= 0 && (xp == v || xn == v);
+      }
     }
-    return v;
+    return Pids{v, __ballot(sh)};
   };
   uint32_t t0 = blockIdx.x * (blockDim.x / kWave) + uniform(threadIdx.x / kWave);
   ItemDesc d0 = decode_item(load_item(p, item_of(t0)));
   RawItem r1 = load_item(p, item_of(t0 + nw));
-  int pid0 = fetch_pids(d0);
+  Pids pid0 = fetch_pids(d0);
 
   for (; t0 < units; t0 += nw) {
     // ---- run-ahead for the following units (fixed position, unconditional)
     const RawItem r2 = load_item(p, item_of(t0 + 2 * nw));
     const ItemDesc d1 = decode_item(r1);
-    const int pid1 = fetch_pids(d1);
+    const Pids pid1 = fetch_pids(d1);
 
     const int rem = int(t0 % uint32_t(UPI));
     const int h = rem / NHB, hb = rem % NHB;
@@ -876,22 +935,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KV4_WAVES_P
         const int r0 = i * kPage;
         return range_mask(0 - r0, se - r0) | range_mask(S - r0, S + nring - r0);
       };
-      run_tiles<kInt8Tile, D, KV4_STAGES8, Q8>(u, ntiles, ptr, mask, lane, setup);
+      run_tiles<kInt8Tile, D, KV4_STAGES8, Q8, false>(u, ntiles, ptr, mask, lane, setup);
     }
 
     // ---- middle pages of this item (at most 64: one page id per lane)
     if (d.npg > 0) {
+      constexpr int ST = MAIN == kInt4Page ? KV4_STAGES : (MAIN == kInt8Tile ? KV4_STAGES8 : 1);
+      // pages [0, ns) of the item are shared with a neighbouring sequence
+      const int ns = ~pid0.shared == 0ull ? kWave : int(__builtin_ctzll(~pid0.shared));
       auto ptr = [&](int i) {
-        const int pid = __builtin_amdgcn_readlane(pid0, i);
+        const int pid = __builtin_amdgcn_readlane(pid0.pid, i);
         return p.pages + (int64_t(pid < 0 ? 0 : pid) * H + h) * p.block_bytes;
       };
       auto mask = [&](int i) {
-        const int pid = __builtin_amdgcn_readlane(pid0, i);
+        const int pid = __builtin_amdgcn_readlane(pid0.pid, i);
         const int p0 = (d.first + i) * kPage;
         return pid < 0 ? 0u : range_mask(g.mb - p0, g.me - p0);
       };
-      run_tiles<MAIN, D, MAIN == kInt4Page ? KV4_STAGES : (MAIN == kInt8Tile ? KV4_STAGES8 : 1), Q8>(u, d.npg, ptr,
-                                                                                                   mask, lane, setup);
+      if constexpr (MAIN == kInt4Page && KV4_NT_LOADS) {
+        run_tiles<MAIN, D, ST, Q8, false>(u, ns, ptr, mask, lane, setup);
+        run_tiles<MAIN, D, ST, Q8, true>(
+            u, d.npg - ns, [&](int i) { return ptr(ns + i); }, [&](int i) { return mask(ns + i); }, lane, setup);
+      } else {
+        run_tiles<MAIN, D, ST, Q8, false>(u, d.npg, ptr, mask, lane, setup);
+      }
     }
 
     // ---- finish: per-head denominators, then output or partial

@@ -156,6 +156,22 @@ def test_config2_full_size_bench_launch(kv4):
     _check_all(wl, sample)
 
 
+@pytest.mark.parametrize("int8_query", [False, True], ids=["bf16q", "int8q"])
+def test_shared_prompt_pages(kv4, int8_query):
+    """Two prompt groups of 8 at the config-2 shapes, with lengths that put
+    the end of the INT4 region before, at and after the end of the shared
+    prompt pages (an odd number of them).  Shared pages and private pages are
+    read on different load paths; every sequence is checked in full."""
+    from harness import build_config
+
+    lengths = np.array([257, 300, 383, 384, 385, 512, 529, 1000,
+                        400, 700, 1500, 2049, 271, 640, 900, 3000], dtype=np.int32)
+    wl = build_config(2, kv4.FMT_KV4, keep_inputs=True, lengths=lengths, int8_query=int8_query)
+    wl.step_append()
+    _run(kv4, wl)
+    _check_all(wl)
+
+
 # ---- the integer query-key path (KV4_LAYOUT_INT8_QUERY) ----------------------
 def test_int8_query_config0_and_edges(kv4):
     from harness import build_from_host
