@@ -23,10 +23,12 @@
 //   PV  A = p * v_scale for row m (its group's scale), K = 32 positions,
 //       B = V codes of 16 channels; row m is used only for channels of its
 //       group.  p is split into bf16 hi + lo so the product keeps ~16 bits.
-// INT4 codes enter the MFMA as the exact bf16 value 1 + (code + 8)/16 (two
-// bit operations per pair of codes); the constant part is removed through
-// the accumulator input (-1.5 * sum of the other operand), which leaves
-// sum(x * code) / 16 exactly up to fp32 rounding.
+// INT4 codes enter the MFMA as the exact bf16 value 1 + (code + 8)/128: the
+// nibble becomes the low four mantissa bits, one bit operation per pair of
+// codes plus a shift for all but the lowest nibble pair of a word.  The
+// constant part is removed through the accumulator input (-(1 + 8/128) times
+// the sum of the other operand), which leaves sum(x * code) / 128 exactly up
+// to fp32 rounding.
 #include "kv4_common.h"
 #include "kv4_launch.h"
 
@@ -103,11 +105,22 @@ __device__ inline float max3(float a, float b, float c) {
 }
 __device__ inline float sbyte(uint32_t w, int k) { return float(int32_t(w << (24 - 8 * k)) >> 24); }
 
-// INT4: nibbles k and k+4 of d -> bf16 pair 1 + (code+8)/16.
+// INT4 encoding: code c -> bf16 1 + (c + 8)/kEnc, nibble at mantissa bit kEncShift.
+#ifndef KV4_ENC_SHIFT
+#define KV4_ENC_SHIFT 0
+#endif
+constexpr int kEncShift = KV4_ENC_SHIFT;
+constexpr float kEnc = float(1 << (7 - kEncShift));          // 128
+constexpr float kEncConst = 1.0f + 8.0f / kEnc;              // 1.0625
+constexpr uint32_t kEncMask = 0x000F000Fu << kEncShift;
+constexpr uint32_t kEncBits = (0x3F80u | (8u << kEncShift)) * 0x00010001u;  // 1.0 with the sign bit of the code flipped
+
+// INT4: nibbles k and k+4 of d -> bf16 pair 1 + (code+8)/kEnc.
 template <int K>
 __device__ inline uint32_t nib_pair(uint32_t d) {
-  const uint32_t x = K == 0 ? (d << 3) : (d >> (4 * K - 3));
-  return (x & 0x00780078u) ^ 0x3FC03FC0u;
+  constexpr int sh = 4 * K - kEncShift;
+  const uint32_t x = sh == 0 ? d : (sh < 0 ? (d << -sh) : (d >> sh));
+  return (x & kEncMask) ^ kEncBits;
 }
 __device__ inline uint32_t nib_pair_at(uint32_t d, int k) {  // k in 0..3 (unrolled)
   switch (k) {
@@ -276,7 +289,7 @@ struct Unit {
 };
 
 // QK for one tile -> x[e] = per-group partial score of position 4kg+e, before
-// the softmax scale (and, for INT4, before the factor 16 of the encoding).
+// the softmax scale (and, for INT4, before the factor kEnc of the encoding).
 template <int KIND, int D, bool Q8>
 __device__ inline void qk_tile(const Unit<D>& u, const Tile<KIND, D>& T, float (&x)[4]) {
   constexpr int NG = D / 32;
@@ -308,7 +321,7 @@ __device__ inline void qk_tile(const Unit<D>& u, const Tile<KIND, D>& T, float (
     }
     acc = f32x4_t{float(ai[0]), float(ai[1]), float(ai[2]), float(ai[3])};
   } else if constexpr (KIND == kInt4Page) {
-    const float c = -1.5f * u.qsum;
+    const float c = -kEncConst * u.qsum;
     acc = f32x4_t{c, c, c, c};
 #pragma unroll
     for (int t = 0; t < NG; ++t) {
@@ -405,8 +418,8 @@ __device__ inline void step(Unit<D>& u, const Tile<KIND, D>& T0, const Tile<KIND
     }
   }
   float mx = max3(max3(x0[0], x0[1], x0[2]), max3(x0[3], x1[0], x1[1]), max3(x1[2], x1[3], -INFINITY));
-  // score (log2 units) = sc * x; INT4 partials carry the encoding's 1/16
-  const float sc = (KIND == kInt4Page && !Q8) ? 16.0f * u.qk_scale : u.qk_scale;
+  // score (log2 units) = sc * x; INT4 partials carry the encoding's 1/kEnc
+  const float sc = (KIND == kInt4Page && !Q8) ? kEnc * u.qk_scale : u.qk_scale;
 
   // The running max of a head is only re-referenced when a score exceeds it
   // by 2^kRescale (then to the head's exact maximum so far), so p <= 2^8 and
@@ -439,11 +452,11 @@ __device__ inline void step(Unit<D>& u, const Tile<KIND, D>& T0, const Tile<KIND
   u.l += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
 
   // A operand of PV: p * v_scale of (position, this row's group), split into
-  // bf16 hi + lo.  INT8 and bf16 rows carry the 1/16 of the INT4 encoding.
+  // bf16 hi + lo.  INT8 and bf16 rows carry the 1/kEnc of the INT4 encoding.
   float ap[8];
   if constexpr (KIND == kBf16Page) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) ap[e] = pr[e] * 0.0625f;
+    for (int e = 0; e < 8; ++e) ap[e] = pr[e] * (1.0f / kEnc);
   } else {
     ap[0] = mul_h_lo(pr[0], T0.vs[0]);
     ap[1] = mul_h_hi(pr[1], T0.vs[0]);
@@ -455,7 +468,7 @@ __device__ inline void step(Unit<D>& u, const Tile<KIND, D>& T0, const Tile<KIND
     ap[7] = mul_h_hi(pr[7], T1.vs[1]);
     if constexpr (KIND != kInt4Page) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) ap[e] *= 0.0625f;
+      for (int e = 0; e < 8; ++e) ap[e] *= (1.0f / kEnc);
     }
   }
   uint32_t hi[4], lo[4];
@@ -470,9 +483,10 @@ __device__ inline void step(Unit<D>& u, const Tile<KIND, D>& T0, const Tile<KIND
   const bf16x8_t a_lo = bf8(lo[0], lo[1], lo[2], lo[3]);
 
   if constexpr (KIND == kInt4Page) {
-    // -1.5 * sum over the positions of this row's A: the constant part of the
-    // 1 + (code+8)/16 encoding of the V codes, added to the output at the end.
-    const bf16x8_t ones = bf8(0xBFC0BFC0u, 0xBFC0BFC0u, 0xBFC0BFC0u, 0xBFC0BFC0u);
+    // -(1 + 8/kEnc) * sum over the positions of this row's A: the constant
+    // part of the V codes' encoding, added to the output at the end.
+    constexpr uint32_t kNeg = (0xBF80u | (8u << kEncShift)) * 0x00010001u;
+    const bf16x8_t ones = bf8(kNeg, kNeg, kNeg, kNeg);
     u.corr = mfma(a_hi, ones, u.corr);
     u.corr = mfma(a_lo, ones, u.corr);
   }
@@ -979,10 +993,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KV4_WAVES_P
           const int c = 16 * t + ln;
           const float o = u.o[t][e] + u.corr[e];
           if (d.nitems == 1) {
-            const float v = lh > 0.f ? 16.0f * o / lh : 0.f;
+            const float v = lh > 0.f ? kEnc * o / lh : 0.f;
             p.out[(int64_t(b) * Hq + hq) * D + c] = f32_to_bf16_bits(v);
           } else {
-            p.ws.partials[(pslot * Hq + hq) * (D + 2) + c] = 16.0f * o;
+            p.ws.partials[(pslot * Hq + hq) * (D + 2) + c] = kEnc * o;
           }
         }
       }
