@@ -203,7 +203,7 @@ def cpu_baseline(wl, budget_s=12.0, max_seqs=256):
 
 def read_probe_gbs(nbytes=4 << 30, reps=5):
     """Achievable streaming read bandwidth: kv4_hbm_read_probe over `nbytes`
-    (128-bit loads, the same load width as the decode), HIP events."""
+    (128-bit nontemporal loads, contiguous per wave), HIP events."""
     import torch
 
     import int4_kv_cache_amd as kv4

@@ -255,7 +255,8 @@ kv4_status kvbf16_decode_phases(const kv4_layout* layout, const kv4_cache* cache
                                 uint32_t phases, hipStream_t stream);
 
 /* ---- measurement aid ----------------------------------------------------------
- * Streams `bytes` (a multiple of 16) of `buf` through 128-bit loads and
+ * Streams `bytes` (a multiple of 16) of `buf` through 128-bit nontemporal
+ * loads, each wave reading its own contiguous share in whole-KiB pieces, and
  * stores one XOR-folded word per workgroup into `sink` (device,
  * [kv4_probe_blocks] uint32) so the loads are not removed.  Used to measure
  * the achievable HBM read bandwidth; not part of the decode path. */
