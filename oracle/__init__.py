@@ -83,6 +83,9 @@ def lib():
         L.orc_decode.argtypes = [ctypes.c_int, P, P, i64, P, i32, P, i32, P, P, i32, P,
                                  ctypes.c_double, P, i32, P, P, P, i32, i32]
         L.orc_decode.restype = ctypes.c_int
+        L.orc_decode_mq.argtypes = [ctypes.c_int, P, P, i64, P, i32, P, i32, P, P, i32, P, i32,
+                                    ctypes.c_double, P, i32, P, P, P, i32]
+        L.orc_decode_mq.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -225,4 +228,31 @@ def decode(cache: HostCache, page_table, seq_lens, slot_ids, q_bf16, sm_scale=1.
                           int(nthreads), 1 if q_int8 else 0)
     if rc != 0:
         raise ValueError(f"oracle decode rejected its input (code {rc})")
+    return out, lse, float(gap[0])
+
+
+def decode_mq(cache: HostCache, page_table, seq_lens, slot_ids, q_bf16, num_queries: int,
+              sm_scale=1.0, subset=None, nthreads=0):
+    """Multi-query decode: q_bf16 [B][T][Hq][D]; returns (out[n][T][Hq][D] fp64,
+    lse[n][T][Hq] fp64, max merge gap).  Query t of sequence b sees the first
+    seq_lens[b] - T + t + 1 positions of the cache as it stands."""
+    lay = cache.lay
+    T = int(num_queries)
+    pt = np.ascontiguousarray(page_table, dtype=np.int32)
+    sl = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    si = None if slot_ids is None else np.ascontiguousarray(slot_ids, dtype=np.int32)
+    q = np.ascontiguousarray(q_bf16, dtype=np.uint16)
+    assert q.size == sl.size * T * lay.num_q_heads * lay.head_dim
+    sub = None if subset is None else np.ascontiguousarray(subset, dtype=np.int32)
+    nseq = sl.size if sub is None else sub.size
+    out = np.zeros((nseq, T, lay.num_q_heads, lay.head_dim), dtype=np.float64)
+    lse = np.zeros((nseq, T, lay.num_q_heads), dtype=np.float64)
+    gap = np.zeros(1, dtype=np.float64)
+    rc = lib().orc_decode_mq(cache.fmt, ctypes.byref(lay), _ptr(cache.pages), cache.num_pages,
+                             _ptr(cache.side), cache.num_slots, _ptr(pt), pt.shape[1], _ptr(sl),
+                             _ptr(si), sl.size, _ptr(q), T, float(sm_scale), _ptr(sub),
+                             0 if sub is None else sub.size, _ptr(out), _ptr(lse), _ptr(gap),
+                             int(nthreads))
+    if rc != 0:
+        raise ValueError(f"oracle multi-query decode rejected its input (code {rc})")
     return out, lse, float(gap[0])

@@ -566,3 +566,68 @@ int orc_decode(int fmt, const orc_layout* L, const uint8_t* pages,
   *max_gap = gap_all;
   return status;
 }
+
+/* Multi-query decode (a reading of this library: the pages describe the
+ * single-token step).  Query t of sequence b sits at position N - T + t of a
+ * cache holding N = seq_lens[b] positions and sees the first
+ * n_t = N - T + t + 1 of them, each read from where the cache holds it after
+ * the append: the side cache for sinks and for the positions the ring still
+ * holds, the INT4 pages for the rest ([NEWS] Interpretation para 3).  That is
+ * exactly a prefix of the rows orc_gather returns for the whole cache, so
+ * every query attends over the first n_t gathered rows. */
+int orc_decode_mq(int fmt, const orc_layout* L, const uint8_t* pages,
+                  int64_t num_pages, const uint8_t* side, int32_t num_slots,
+                  const int32_t* page_table, int32_t max_pages,
+                  const int32_t* seq_lens, const int32_t* slot_ids, int32_t batch,
+                  const uint16_t* q, int32_t T, double sm, const int32_t* subset,
+                  int32_t n_subset, double* out, double* lse, double* max_gap,
+                  int32_t nthreads) {
+  if (!layout_ok(L) || T < 1) return -1;
+  int D = L->head_dim, H = L->num_kv_heads, Hq = L->num_q_heads, g = Hq / H;
+  int nseq = subset ? n_subset : batch;
+  int nwork = nseq * H;
+  int status = 0;
+  double gap_all = 0.0;
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 1) reduction(max : gap_all) reduction(min : status)
+#endif
+  for (int w = 0; w < nwork; ++w) {
+    int i = w / H, h = w % H;
+    int b = subset ? subset[i] : i;
+    if (b < 0 || b >= batch) {
+      status = -5;
+      continue;
+    }
+    int N = seq_lens[b];
+    size_t rows = N > 0 ? (size_t)N : 1;
+    double* K = (double*)malloc(sizeof(double) * rows * D);
+    double* V = (double*)malloc(sizeof(double) * rows * D);
+    uint8_t* reg = (uint8_t*)malloc(rows);
+    int rc = orc_gather(fmt, L, pages, num_pages, side, num_slots, page_table,
+                        max_pages, seq_lens, slot_ids, b, h, K, V, reg);
+    if (rc < 0) {
+      status = rc;
+    } else {
+      for (int t = 0; t < T; ++t) {
+        int n = N - T + t + 1;
+        if (n < 0) n = 0;
+        for (int j = 0; j < g; ++j) {
+          int hq = h * g + j;
+          double qv[128];
+          const uint16_t* qrow = q + (((size_t)b * T + t) * Hq + hq) * D;
+          for (int c = 0; c < D; ++c) qv[c] = (double)orc_bf16_to_f32(qrow[c]);
+          double gap;
+          size_t o = ((size_t)i * T + t) * Hq + hq;
+          orc_attend(n, D, qv, K, V, reg, sm, out + o * D, lse + o, &gap);
+          if (gap > gap_all) gap_all = gap;
+        }
+      }
+    }
+    free(K);
+    free(V);
+    free(reg);
+  }
+  *max_gap = gap_all;
+  return status;
+}

@@ -122,6 +122,18 @@ int orc_decode(int fmt, const orc_layout* L, const uint8_t* pages,
                int32_t n_subset, double* out, double* lse, double* max_gap,
                int32_t nthreads, int32_t q_int8);
 
+/* Multi-query decode: T query tokens per sequence (q [batch][T][Hq][D]);
+ * query t of sequence b sees the first N - T + t + 1 positions of the cache
+ * as it stands (N = seq_lens[b]), each read from where the cache holds it.
+ * out[i][T][Hq][D], lse[i][T][Hq]; queries that see no position give 0 and
+ * -inf.  T = 1 is orc_decode with q_int8 = 0. */
+int orc_decode_mq(int fmt, const orc_layout* L, const uint8_t* pages,
+                  int64_t num_pages, const uint8_t* side, int32_t num_slots,
+                  const int32_t* page_table, int32_t max_pages,
+                  const int32_t* seq_lens, const int32_t* slot_ids, int32_t batch,
+                  const uint16_t* q, int32_t T, double sm_scale,
+                  const int32_t* subset, int32_t n_subset, double* out,
+                  double* lse, double* max_gap, int32_t nthreads);
 #ifdef __cplusplus
 }
 #endif

@@ -12,5 +12,6 @@ from .gen import (  # noqa: F401
     outlier_channels,
     host_sequence,
     host_prompt,
+    host_queries,
     PageAllocator,
 )

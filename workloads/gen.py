@@ -84,6 +84,14 @@ def host_prompt(cfg: Config, layer: int, group: int):
     return bf16_bits_from_f32(K), bf16_bits_from_f32(V)
 
 
+def host_queries(cfg: Config, layer: int, batch: int, n_queries: int):
+    """bf16 bits q [batch][n_queries][Hq][D] for multi-query decode."""
+    rng = np.random.default_rng([cfg.seed, layer, 2 * 10**6 + n_queries])
+    q = rng.standard_normal((batch, n_queries, cfg.num_q_heads, cfg.head_dim), dtype=np.float32)
+    q *= np.float32(1.0 / math.sqrt(cfg.head_dim))
+    return bf16_bits_from_f32(q)
+
+
 # -------------------------------------------------------------- device data ---
 def device_tokens(cfg: Config, layer: int, stream: int, n_tokens: int, device,
                   chunk: int = 1 << 20):
@@ -106,13 +114,15 @@ def device_tokens(cfg: Config, layer: int, stream: int, n_tokens: int, device,
     return K, V
 
 
-def device_queries(cfg: Config, layer: int, batch: int, device):
+def device_queries(cfg: Config, layer: int, batch: int, device, n_queries: int = 0):
+    """bf16 q [batch][Hq][D], or [batch][n_queries][Hq][D] when n_queries > 0."""
     import torch
 
     g = torch.Generator(device=device)
-    g.manual_seed(int(cfg.seed) * 1_000_003 + int(layer) * 10_007 + 999_983)
-    q = torch.randn((batch, cfg.num_q_heads, cfg.head_dim), generator=g, device=device,
-                    dtype=torch.float32) / math.sqrt(cfg.head_dim)
+    g.manual_seed(int(cfg.seed) * 1_000_003 + int(layer) * 10_007 + 999_983 + 7 * n_queries)
+    shape = (batch, cfg.num_q_heads, cfg.head_dim) if n_queries <= 0 else \
+        (batch, n_queries, cfg.num_q_heads, cfg.head_dim)
+    q = torch.randn(shape, generator=g, device=device, dtype=torch.float32) / math.sqrt(cfg.head_dim)
     return q.to(torch.bfloat16)
 
 
