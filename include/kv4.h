@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define KV4_ABI_VERSION 2
+#define KV4_ABI_VERSION 3
 
 typedef enum {
   KV4_OK = 0,
@@ -253,6 +253,44 @@ kv4_status kvbf16_decode_phases(const kv4_layout* layout, const kv4_cache* cache
                                 float softmax_scale, uint16_t* out, float* lse,
                                 void* workspace, size_t workspace_bytes,
                                 uint32_t phases, hipStream_t stream);
+
+/* ---- multi-query decode ------------------------------------------------------
+ * T = num_queries query tokens per sequence (1 <= T <= KV4_MAX_QUERIES): the
+ * last T positions of each context, already appended.  Query t of sequence b
+ * sits at position N - T + t (N = seq_lens[b]) and attends causally to the
+ * n = N - T + t + 1 positions [0, n) of the cache as it stands after the
+ * append: sinks [0, min(S, n)) and the positions the ring holds,
+ * [max(S, N - R), N) within [0, n), from the INT8 side cache; the rest of
+ * [S, n) from the INT4 pages.  Regions are merged exactly as in
+ * kv4_decode_attention, which this is for T = 1.  The pages describe the
+ * single-token decode step; running several query tokens over one cache
+ * state (speculative verification, chunked prefill over the cache) is a
+ * reading of this library.
+ *   q      bf16 [batch][T][num_q_heads][head_dim]
+ *   out    bf16 [batch][T][num_q_heads][head_dim]
+ *   lse    fp32 [batch][T][num_q_heads], or NULL
+ * Queries with n <= 0 (T > N) give out = 0 and lse = -inf.  The workspace
+ * is kv4_decode_workspace_size(layout, batch * T, max_pages); the 2^31-unit
+ * bound of kv4_decode_attention applies to batch * T sequences.  Each query
+ * reads the cache on its own (T reads of the shared positions; queries of
+ * one sequence are scheduled next to each other so that the repeats are
+ * served from the caches). */
+#define KV4_MAX_QUERIES 64
+kv4_status kv4_decode_attention_mq(const kv4_layout* layout, const kv4_cache* cache,
+                                   const kv4_batch* batch, const uint16_t* q,
+                                   int32_t num_queries, float softmax_scale,
+                                   uint16_t* out, float* lse, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream);
+kv4_status kv8_decode_attention_mq(const kv4_layout* layout, const kv4_cache* cache,
+                                   const kv4_batch* batch, const uint16_t* q,
+                                   int32_t num_queries, float softmax_scale,
+                                   uint16_t* out, float* lse, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream);
+kv4_status kvbf16_decode_attention_mq(const kv4_layout* layout, const kv4_cache* cache,
+                                      const kv4_batch* batch, const uint16_t* q,
+                                      int32_t num_queries, float softmax_scale,
+                                      uint16_t* out, float* lse, void* workspace,
+                                      size_t workspace_bytes, hipStream_t stream);
 
 /* ---- measurement aid ----------------------------------------------------------
  * Streams `bytes` (a multiple of 16) of `buf` through 128-bit nontemporal

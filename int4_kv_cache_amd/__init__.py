@@ -59,6 +59,7 @@ EXPORTS = [
     "kv4_decode_workspace_size",
     "kv4_decode_attention", "kv8_decode_attention", "kvbf16_decode_attention",
     "kv4_decode_phases", "kv8_decode_phases", "kvbf16_decode_phases",
+    "kv4_decode_attention_mq", "kv8_decode_attention_mq", "kvbf16_decode_attention_mq",
     "kv4_probe_blocks", "kv4_hbm_read_probe",
 ]
 
@@ -92,6 +93,9 @@ def load(path: Optional[str] = None):
         f = getattr(L, f"{pre}_decode_phases")
         f.restype = ctypes.c_int
         f.argtypes = [P, P, P, P, ctypes.c_float, P, P, P, sz, ctypes.c_uint32, P]
+        f = getattr(L, f"{pre}_decode_attention_mq")
+        f.restype = ctypes.c_int
+        f.argtypes = [P, P, P, P, i32, ctypes.c_float, P, P, P, sz, P]
     L.kv4_decode_workspace_size.restype = ctypes.c_int
     L.kv4_decode_workspace_size.argtypes = [P, i32, i32, ctypes.POINTER(sz)]
     L.kv4_probe_blocks.restype = i32
@@ -203,6 +207,22 @@ def decode(cache: Cache, batch: Batch, q, out, lse, workspace, softmax_scale: fl
     st = getattr(load(), fn)(ctypes.byref(lay), ctypes.byref(cd), ctypes.byref(bd), _ptr(q),
                              float(softmax_scale), _ptr(out), _ptr(lse), _ptr(workspace),
                              int(workspace.numel()), _stream(stream))
+    _check(fn, st)
+
+
+MAX_QUERIES = 64
+
+
+def decode_mq(cache: Cache, batch: Batch, q, num_queries: int, out, lse, workspace,
+              softmax_scale: float = 1.0, stream=None):
+    """Multi-query decode: q/out bf16 [B][T][Hq][D], lse fp32 [B][T][Hq] (or None);
+    query t of sequence b sees positions [0, seq_lens[b] - T + t + 1).  The
+    workspace is workspace_size(layout, B * T, max_pages)."""
+    fn = f"{_PREFIX[cache.fmt]}_decode_attention_mq"
+    lay, cd, bd = cache.layout, cache.desc(), batch.desc()
+    st = getattr(load(), fn)(ctypes.byref(lay), ctypes.byref(cd), ctypes.byref(bd), _ptr(q),
+                             int(num_queries), float(softmax_scale), _ptr(out), _ptr(lse),
+                             _ptr(workspace), int(workspace.numel()), _stream(stream))
     _check(fn, st)
 
 

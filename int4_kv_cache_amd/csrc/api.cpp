@@ -93,8 +93,9 @@ kv4_status append_impl(int fmt, const kv4_layout* L, const kv4_cache* c, const k
 
 kv4_status decode_impl(int fmt, const kv4_layout* L, const kv4_cache* c, const kv4_batch* b,
                        const uint16_t* q, float sm, uint16_t* out, float* lse, void* ws, size_t ws_bytes,
-                       unsigned phases, hipStream_t stream) {
+                       unsigned phases, hipStream_t stream, int32_t nq = 1) {
   if (phases < 1u || phases > 7u) return KV4_ERR_INVALID_ARG;
+  if (nq < 1 || nq > KV4_MAX_QUERIES) return KV4_ERR_INVALID_ARG;
   kv4_status s = layout_check(L, fmt);
   if (s != KV4_OK) return s;
   if (!b) return KV4_ERR_INVALID_ARG;
@@ -111,9 +112,12 @@ kv4_status decode_impl(int fmt, const kv4_layout* L, const kv4_cache* c, const k
   if ((phases & (KV4_PHASE_ATTEND | KV4_PHASE_MERGE)) && !out) return KV4_ERR_INVALID_ARG;
   if ((phases & KV4_PHASE_ATTEND) && !q) return KV4_ERR_INVALID_ARG;
   if (!(sm > 0.0f) || sm > 3.0e38f) return KV4_ERR_INVALID_ARG;  // positive and finite
-  if (!kv4::decode_units_fit(b->batch, b->max_pages, L->num_q_heads, L->num_kv_heads, L->head_dim))
+  // the kernels index work by b * nq + t
+  if (int64_t(b->batch) * nq > int64_t(INT32_MAX)) return KV4_ERR_UNSUPPORTED;
+  const int32_t nv = b->batch * nq;
+  if (!kv4::decode_units_fit(nv, b->max_pages, L->num_q_heads, L->num_kv_heads, L->head_dim))
     return KV4_ERR_UNSUPPORTED;
-  const size_t need = kv4::decode_workspace_bytes(b->batch, b->max_pages, L->num_q_heads, L->head_dim);
+  const size_t need = kv4::decode_workspace_bytes(nv, b->max_pages, L->num_q_heads, L->head_dim);
   if (ws_bytes < need) return KV4_ERR_WORKSPACE;
   kv4::DecodeParams p{};
   if (c) {
@@ -127,6 +131,7 @@ kv4_status decode_impl(int fmt, const kv4_layout* L, const kv4_cache* c, const k
   p.seq_lens = b->seq_lens;
   p.slot_ids = b->slot_ids;
   p.batch = b->batch;
+  p.nq = nq;
   p.q = q;
   p.softmax_scale = sm;
   p.out = out;
@@ -137,7 +142,7 @@ kv4_status decode_impl(int fmt, const kv4_layout* L, const kv4_cache* c, const k
   p.n_recent = fmt == kFmtKV4 ? L->n_recent : 0;
   p.block_bytes = int64_t(block_bytes(L, fmt));
   p.side_bytes = int64_t(side_bytes(L));
-  p.ws = kv4::carve_workspace(ws, b->batch, b->max_pages, L->num_q_heads, L->head_dim);
+  p.ws = kv4::carve_workspace(ws, nv, b->max_pages, L->num_q_heads, L->head_dim);
   if (!protected_set(L, fmt)) {
     p.side = nullptr;
     p.num_slots = 0;
@@ -224,6 +229,22 @@ kv4_status kvbf16_decode_phases(const kv4_layout* L, const kv4_cache* c, const k
                                 float sm, uint16_t* out, float* lse, void* ws, size_t ws_bytes, uint32_t phases,
                                 hipStream_t stream) {
   return decode_impl(kFmtBF16, L, c, b, q, sm, out, lse, ws, ws_bytes, phases, stream);
+}
+
+kv4_status kv4_decode_attention_mq(const kv4_layout* L, const kv4_cache* c, const kv4_batch* b,
+                                   const uint16_t* q, int32_t num_queries, float sm, uint16_t* out, float* lse,
+                                   void* ws, size_t ws_bytes, hipStream_t stream) {
+  return decode_impl(kFmtKV4, L, c, b, q, sm, out, lse, ws, ws_bytes, kAllPhases, stream, num_queries);
+}
+kv4_status kv8_decode_attention_mq(const kv4_layout* L, const kv4_cache* c, const kv4_batch* b,
+                                   const uint16_t* q, int32_t num_queries, float sm, uint16_t* out, float* lse,
+                                   void* ws, size_t ws_bytes, hipStream_t stream) {
+  return decode_impl(kFmtKV8, L, c, b, q, sm, out, lse, ws, ws_bytes, kAllPhases, stream, num_queries);
+}
+kv4_status kvbf16_decode_attention_mq(const kv4_layout* L, const kv4_cache* c, const kv4_batch* b,
+                                      const uint16_t* q, int32_t num_queries, float sm, uint16_t* out,
+                                      float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return decode_impl(kFmtBF16, L, c, b, q, sm, out, lse, ws, ws_bytes, kAllPhases, stream, num_queries);
 }
 
 int32_t kv4_probe_blocks(void) { return kv4::probe_blocks(); }

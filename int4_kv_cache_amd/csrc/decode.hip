@@ -576,25 +576,36 @@ constexpr int kMaxChunkPages = 64;  // one lane per page id of an item
 constexpr int kProtectedCost = 2;    // an INT8 tile costs about two INT4 pages
 
 struct SeqWork {
-  int L;           // context length (clamped to the page table)
+  int L;           // positions the query sees: [0, L)
+  int N;           // positions in the cache (clamped to the page table)
   int mid_first;   // first / last page holding middle rows (last < first: none)
   int mid_last;
   int prot_tiles;  // INT8 side tiles holding protected rows
 };
 
-__device__ inline SeqWork seq_work(const DecodeParams& p, int b) {
+// Side rows a query reads: the sinks it sees, and when it sees any ring
+// position the whole written ring (its other rows are masked).
+__device__ inline int side_rows(int L, int N, int S, int R) {
+  const Regions g = regions_in(L, N, S, R);
+  const int nring = N > S ? (N - S < R ? N - S : R) : 0;
+  return L > g.rb ? S + nring : g.se;
+}
+
+// Work index v = b * nq + t: query t of sequence b sits at position N - nq + t
+// and sees positions [0, N - nq + t + 1).
+__device__ inline SeqWork seq_work(const DecodeParams& p, int v) {
   SeqWork w;
-  int L = p.seq_lens[b];
-  L = L < 0 ? 0 : (L > p.max_pages * kPage ? p.max_pages * kPage : L);
+  const int b = v / p.nq, t = v - b * p.nq;
+  int N = p.seq_lens[b];
+  N = N < 0 ? 0 : (N > p.max_pages * kPage ? p.max_pages * kPage : N);
+  int L = N - p.nq + 1 + t;
+  L = L < 0 ? 0 : L;
   w.L = L;
-  const Regions g = regions(L, p.n_sink, p.n_recent);
+  w.N = N;
+  const Regions g = regions_in(L, N, p.n_sink, p.n_recent);
   w.mid_first = g.mb / kPage;
   w.mid_last = g.me > g.mb ? (g.me - 1) / kPage : w.mid_first - 1;
-  const int S = p.n_sink, R = p.n_recent;
-  const int se = L < S ? L : S;
-  const int nring = L > S ? (L - S < R ? L - S : R) : 0;
-  const int rows = nring > 0 ? S + nring : se;
-  w.prot_tiles = (rows + kPage - 1) / kPage;
+  w.prot_tiles = (side_rows(L, N, p.n_sink, p.n_recent) + kPage - 1) / kPage;
   return w;
 }
 
@@ -609,13 +620,14 @@ __device__ inline int item_pages(const SeqWork& w, int chunk, int k) {
 }
 
 // Work-item descriptor, two int4:
-//   [0] = {b, L, first middle page of the item, (chunk index << 8) | pages}
-//   [1] = {items of b, first partial slot of b, side slot, 0}
-__device__ inline void write_item(const DecodeParams& p, uint32_t pos, int b, const SeqWork& w, int chunk, int k,
+//   [0] = {v, L, first middle page of the item, (chunk index << 8) | pages}
+//   [1] = {items of v, first partial slot of v, side slot, N}
+__device__ inline void write_item(const DecodeParams& p, uint32_t pos, int v, const SeqWork& w, int chunk, int k,
                                   int n, int pbase) {
+  const int b = v / p.nq;
   const int slot = p.slot_ids ? p.slot_ids[b] : b;
-  p.ws.items[2 * pos] = make_int4(b, w.L, w.mid_first + k * chunk, (k << 8) | item_pages(w, chunk, k));
-  p.ws.items[2 * pos + 1] = make_int4(n, pbase, slot, 0);
+  p.ws.items[2 * pos] = make_int4(v, w.L, w.mid_first + k * chunk, (k << 8) | item_pages(w, chunk, k));
+  p.ws.items[2 * pos + 1] = make_int4(n, pbase, slot, w.N);
 }
 
 // Block-wide helpers of the work-list kernel (1024 threads = 16 waves).
@@ -659,12 +671,13 @@ __global__ __launch_bounds__(1024) void worklist_kernel(DecodeParams p, int unit
   __shared__ uint32_t bucket[kMaxChunkPages + 2];
   __shared__ uint32_t nmerge;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
+  const int nv = p.batch * p.nq;  // work indices b * nq + t
   for (int i = tid; i < kMaxChunkPages + 2; i += 1024) bucket[i] = 0u;
   if (tid == 0) nmerge = 0u;
   SeqWork w0{};
-  if (tid < p.batch) w0 = seq_work(p, tid);
+  if (tid < nv) w0 = seq_work(p, tid);
   unsigned long long mine = 0ull;
-  for (int b = tid; b < p.batch; b += 1024) {
+  for (int b = tid; b < nv; b += 1024) {
     const SeqWork w = b == tid ? w0 : seq_work(p, b);
     mine += unsigned(mid_pages(w)) + unsigned(kProtectedCost * w.prot_tiles);
   }
@@ -678,10 +691,10 @@ __global__ __launch_bounds__(1024) void worklist_kernel(DecodeParams p, int unit
 
   // pass 1: full items (scan) and the histogram of the other items' sizes
   int run_full = 0, run_split = 0;
-  for (int base = 0; base < p.batch; base += 1024) {
+  for (int base = 0; base < nv; base += 1024) {
     const int b = base + tid;
     int full = 0, split = 0;
-    if (b < p.batch) {
+    if (b < nv) {
       const SeqWork w = base == 0 ? w0 : seq_work(p, b);
       const int n = n_items(w, chunk);
       for (int k = 0; k < n; ++k) {
@@ -694,7 +707,7 @@ __global__ __launch_bounds__(1024) void worklist_kernel(DecodeParams p, int unit
     unsigned long long tile = 0ull;
     const unsigned long long ex =
         block_exclusive_scan((unsigned long long)full | ((unsigned long long)split << 32), part, tile);
-    if (b < p.batch) {
+    if (b < nv) {
       p.ws.item_base[b] = run_split + int(ex >> 32);
       p.ws.merge_list[b] = run_full + int(ex & 0xFFFFFFFFull);  // scratch: first full-item position
     }
@@ -718,7 +731,7 @@ __global__ __launch_bounds__(1024) void worklist_kernel(DecodeParams p, int unit
   }
   __syncthreads();
   // pass 2: descriptors
-  for (int b = tid; b < p.batch; b += 1024) {
+  for (int b = tid; b < nv; b += 1024) {
     const SeqWork w = b == tid ? w0 : seq_work(p, b);
     const int n = n_items(w, chunk);
     const int pbase = p.ws.item_base[b];
@@ -732,7 +745,7 @@ __global__ __launch_bounds__(1024) void worklist_kernel(DecodeParams p, int unit
   }
   __syncthreads();
   // list of split sequences for the merge (overwrites the scratch use above)
-  for (int b = tid; b < p.batch; b += 1024) {
+  for (int b = tid; b < nv; b += 1024) {
     const SeqWork w = b == tid ? w0 : seq_work(p, b);
     if (n_items(w, chunk) > 1) p.ws.merge_list[atomicAdd(&nmerge, 1u)] = b;
   }
@@ -742,7 +755,7 @@ __global__ __launch_bounds__(1024) void worklist_kernel(DecodeParams p, int unit
 
 // ------------------------------------------------------------- attention --
 struct ItemDesc {
-  int b, L, first, ck, npg, nitems, pbase, slot;
+  int b, L, first, ck, npg, nitems, pbase, slot, N;  // b: work index b * nq + t
 };
 
 // A work-item descriptor as loaded (two int4, identical in every lane) and its
@@ -771,6 +784,7 @@ __device__ inline ItemDesc decode_item(const RawItem& r) {
   d.nitems = uniform(r.c.x);
   d.pbase = uniform(r.c.y);
   d.slot = uniform(r.c.z);
+  d.N = uniform(r.c.w);
   return d;
 }
 
@@ -811,12 +825,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KV4_WAVES_P
     int v = 0;
     bool sh = false;
     if (lane < d.npg) {
-      const int64_t at = int64_t(d.b) * p.max_pages + d.first + lane;
-      const int64_t x = p.page_table[at];
+      const int col = d.first + lane;
+      const int64_t x = p.page_table[int64_t(d.b / p.nq) * p.max_pages + col];
       v = (x < 0 || x >= p.num_pages) ? -1 : int(x);
       if constexpr (KV4 && KV4_NT_LOADS) {
-        const int xp = d.b > 0 ? p.page_table[at - p.max_pages] : -1;
-        const int xn = d.b + 1 < p.batch ? p.page_table[at + p.max_pages] : -1;
+        // the neighbouring work indices: other queries of this sequence or
+        // the sequences before and after it
+        const int xp = d.b > 0 ? p.page_table[int64_t((d.b - 1) / p.nq) * p.max_pages + col] : -1;
+        const int xn = d.b + 1 < p.batch * p.nq ? p.page_table[int64_t((d.b + 1) / p.nq) * p.max_pages + col] : -1;
         sh = v >= 0 && (xp == v || xn == v);
       }
     }
@@ -837,7 +853,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KV4_WAVES_P
     const int h = rem / NHB, hb = rem % NHB;
     const ItemDesc d = d0;
     const int b = d.b, L = d.L;
-    const Regions g = regions(L, S, R);
+    const Regions g = regions_in(L, d.N, S, R);
 
     // ---- unit set-up.  The q loads are issued here, but the q operand is
     // built only after the unit's first tile loads are in flight (run_tiles
@@ -939,15 +955,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KV4_WAVES_P
 
     // ---- protected rows: INT8 side-cache tiles (sinks, then the ring)
     if (KV4 && d.ck == 0 && L > 0 && S + R > 0 && d.slot >= 0 && d.slot < p.num_slots) {
-      const int se = L < S ? L : S;
-      const int nring = L > S ? (L - S < R ? L - S : R) : 0;
-      const int rows = nring > 0 ? S + nring : se;
-      const int ntiles = (rows + kPage - 1) / kPage;
+      const int ntiles = (side_rows(L, d.N, S, R) + kPage - 1) / kPage;
+      // the ring rows of the recent positions [g.rb, L): a cyclic run of
+      // L - g.rb rows from row S + (g.rb - S) mod R
+      const int cnt = L - g.rb;
+      const int rs = cnt > 0 ? (g.rb - S) % R : 0;
+      const int r1 = rs + cnt < R ? rs + cnt : R;  // first run [rs, r1)
+      const int r2 = rs + cnt - r1;                // wrapped run [0, r2)
       const uint8_t* sblk = p.side + (int64_t(d.slot) * H + h) * p.side_bytes;
       auto ptr = [&](int i) { return sblk + int64_t(i) * int8_tile_bytes(D); };
       auto mask = [&](int i) {
         const int r0 = i * kPage;
-        return range_mask(0 - r0, se - r0) | range_mask(S - r0, S + nring - r0);
+        return range_mask(0 - r0, g.se - r0) | range_mask(S + rs - r0, S + r1 - r0) |
+               range_mask(S - r0, S + r2 - r0);
       };
       run_tiles<kInt8Tile, D, KV4_STAGES8, Q8, false>(u, ntiles, ptr, mask, lane, setup);
     }

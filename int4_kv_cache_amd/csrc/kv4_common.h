@@ -58,19 +58,25 @@ __host__ __device__ constexpr size_t vb_byte(int D, int r, int c) {
 struct Regions {
   int se, mb, me, rb;
 };
-__host__ __device__ inline Regions regions(int n, int S, int R) {
+// Regions of a query that sees positions [0, n) of a cache holding N >= n
+// positions: sinks [0, se), middle [mb, me) from the INT4 pages, recent
+// [rb, n) from the ring, which holds positions [max(S, N - R), N).
+__host__ __device__ inline Regions regions_in(int n, int N, int S, int R) {
   Regions g;
   g.se = n < S ? n : S;
-  int r0 = (n - R > S) ? n - R : S;
-  g.rb = r0 > n ? n : r0;
-  if (n - R > S) {
+  const int ring0 = N - R > S ? N - R : S;
+  const int cut = n < ring0 ? n : ring0;  // end of the INT4 region
+  if (n > S) {
     g.mb = S;
-    g.me = n - R;
+    g.me = cut;
+    g.rb = cut;
   } else {
-    g.mb = g.me = g.se;
+    g.mb = g.me = g.rb = g.se;
   }
   return g;
 }
+// Regions of a context of length n (its last position is the query).
+__host__ __device__ inline Regions regions(int n, int S, int R) { return regions_in(n, n, S, R); }
 // Side row of protected position p (p < S: sink row; else ring row).
 __host__ __device__ inline int side_row(int p, int S, int R) { return p < S ? p : S + (p - S) % R; }
 

@@ -152,6 +152,21 @@ def decode_metrics(wl, sample, ocache=None, pt=None, lens=None, nthreads=0):
                 n=len(sample))
 
 
+def metrics_from(og, lg, out64, lse64, gap):
+    """Bounds of the module docstring for GPU outputs og (bf16 values as fp64)
+    and lse lg against oracle out64 / lse64 of the same shape."""
+    ref = to_bf16_rne(out64)
+    denom = np.linalg.norm(ref)
+    rel = float(np.linalg.norm(og - ref) / denom) if denom > 0 else float(np.linalg.norm(og - ref))
+    max_abs = float(np.max(np.abs(og - out64))) if og.size else 0.0
+    fin = np.isfinite(lse64)
+    assert np.array_equal(fin, np.isfinite(lg)), "lse finiteness differs"
+    lse_err = float(np.max(np.abs(lg[fin] - lse64[fin]))) if fin.any() else 0.0
+    rel64 = float(np.linalg.norm(og - out64) / max(np.linalg.norm(out64), 1e-300))
+    return dict(rel_l2=rel, max_abs=max_abs, lse_abs=lse_err, rel_l2_vs_fp64=rel64, merge_gap=gap,
+                n=int(out64.shape[0]))
+
+
 def assert_within(m):
     assert m["rel_l2"] <= REL_L2_MAX, m
     assert m["max_abs"] <= MAX_ABS_MAX, m

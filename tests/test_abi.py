@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.kv4_abi_version() == 2
+    assert lib.kv4_abi_version() == 3
     for code, text in kv4.STATUS.items():
         assert lib.kv4_status_string(code).decode() == text
     assert lib.kv4_status_string(12345).decode() == "unknown status"

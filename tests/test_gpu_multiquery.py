@@ -1,0 +1,108 @@
+"""GPU parity of the multi-query decode (kv4_decode_attention_mq and the kv8 /
+kvbf16 variants) against the oracle's multi-query decode on the same bytes.
+
+Query t of sequence b sees the first seq_lens[b] - T + t + 1 positions of the
+cache as it stands after the append (a reading of this library; the pages
+describe the single-token step).  Bounds as in the single-token parity
+tests: rel-L2 1e-3 against the bf16-rounded oracle, max-abs 1e-2 and lse
+1e-4 against fp64.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import parity_util as pu
+from workloads import get_config, host_queries
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_mq(kv4, wl, T, seed_layer=0):
+    import torch
+
+    cfg = wl.cfg
+    B = wl.lengths.size
+    qh = host_queries(cfg, seed_layer, B, T)
+    q = torch.from_numpy(qh.view(np.int16)).to("cuda").view(torch.bfloat16)
+    out = torch.zeros((B, T, cfg.num_q_heads, cfg.head_dim), dtype=torch.bfloat16, device="cuda")
+    lse = torch.zeros((B, T, cfg.num_q_heads), dtype=torch.float32, device="cuda")
+    mp = wl.alloc.page_table.shape[1]
+    ws = torch.empty(kv4.workspace_bytes(wl.layout, B * T, mp), dtype=torch.uint8, device="cuda")
+    kv4.decode_mq(wl.cache, wl.batch, q, T, out, lse, ws)
+    torch.cuda.synchronize()
+    og = pu.bf16_bits_to_f64(out.view(torch.int16).cpu().numpy())
+    lg = lse.cpu().numpy().astype(np.float64)
+    return qh, og, lg
+
+
+def _check(kv4, wl, T, label):
+    sample = np.arange(wl.lengths.size)
+    ocache, pt, lens = pu.compare_bytes(wl, sample)
+    qh, og, lg = _run_mq(kv4, wl, T)
+    out64, lse64, gap = oracle.decode_mq(ocache, pt, lens, None, qh, T)
+    m = pu.metrics_from(og, lg, out64, lse64, gap)
+    print(f"\nmulti-query {label} T={T}: rel_l2={m['rel_l2']:.3e} max_abs={m['max_abs']:.3e} "
+          f"lse={m['lse_abs']:.3e}", flush=True)
+    pu.assert_within(m)
+    # queries that see no position
+    for b, N in enumerate(wl.lengths):
+        for t in range(T):
+            if N - T + t + 1 <= 0:
+                assert np.all(og[b, t] == 0.0) and np.all(np.isneginf(lg[b, t]))
+    return m
+
+
+@pytest.mark.parametrize("fmt", [0, 1, 2], ids=["kv4", "kv8", "bf16"])
+@pytest.mark.parametrize("T", [1, 3, 8])
+def test_multiquery_small(kv4, fmt, T):
+    """D = 64, 4 sinks + 16 recent; lengths below, at and across the
+    protected bounds and shorter than T."""
+    from harness import build_from_host
+
+    lengths = np.array([300, 517, 5, 21, 16, 20, 37, 2, 33, 100], dtype=np.int32)
+    wl = build_from_host(0, fmt, lengths=lengths)
+    _check(kv4, wl, T, f"cfg0 fmt={fmt}")
+
+
+@pytest.mark.parametrize("T", [5, 9, 20])
+def test_multiquery_more_queries_than_ring(kv4, T):
+    """T larger than the ring (R = 4): early queries end before the ring and
+    read their recent positions from INT4."""
+    from harness import build_from_host
+
+    lengths = np.array([64, 29, 11, 90, 7], dtype=np.int32)
+    wl = build_from_host(0, 0, lengths=lengths, n_sink=4, n_recent=4)
+    _check(kv4, wl, T, "cfg0 S=4 R=4")
+
+
+@pytest.mark.parametrize("T", [2, 4])
+def test_multiquery_qwen_shapes(kv4, T):
+    """Hq 32 / Hkv 8 / D 128 with 16 sinks + 128 recent; split sequences (the
+    merge path) and a sequence within the protected set."""
+    from harness import build_from_host
+
+    lengths = np.array([2100, 700, 145, 1000, 290, 60], dtype=np.int32)
+    wl = build_from_host(1, 0, lengths=lengths)
+    _check(kv4, wl, T, "qwen shapes")
+
+
+def test_multiquery_rejects_bad_counts(kv4):
+    import torch
+
+    from harness import build_from_host
+
+    wl = build_from_host(0, 0, lengths=np.array([40, 50], dtype=np.int32))
+    cfg = get_config(0)
+    q = torch.zeros((2, 1, cfg.num_q_heads, cfg.head_dim), dtype=torch.bfloat16, device="cuda")
+    out = torch.zeros_like(q)
+    ws = torch.empty(1 << 20, dtype=torch.uint8, device="cuda")
+    for bad in (0, -1, kv4.MAX_QUERIES + 1):
+        with pytest.raises(kv4.Kv4Error):
+            kv4.decode_mq(wl.cache, wl.batch, q, bad, out, None, ws)
+    # a workspace sized for one query per sequence is too small for eight
+    T = 8
+    q8 = torch.zeros((2, T, cfg.num_q_heads, cfg.head_dim), dtype=torch.bfloat16, device="cuda")
+    small = torch.empty(kv4.workspace_bytes(wl.layout, 2, wl.alloc.page_table.shape[1]), dtype=torch.uint8,
+                        device="cuda")
+    with pytest.raises(kv4.Kv4Error):
+        kv4.decode_mq(wl.cache, wl.batch, q8, T, torch.zeros_like(q8), None, small)
