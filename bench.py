@@ -162,6 +162,49 @@ def time_steps(wl, steps, warmup, append=True):
     return total_ms / steps, ph
 
 
+def time_multi_query(wl, T, steps, warmup, decode_bytes, decode_us):
+    """kv4_decode_attention_mq with T query tokens per sequence over the
+    workload's cache as it stands (the last T positions are the queries).
+    Algorithmic bytes: the single-token decode's (every cache byte once) plus
+    the q / out / lse of the T - 1 extra queries."""
+    import torch
+
+    import int4_kv_cache_amd as kv4
+    from workloads.gen import device_queries
+
+    cfg = wl.cfg
+    B = int(wl.lengths.size)
+    q = device_queries(cfg, 0, B, "cuda", n_queries=T)
+    out = torch.empty((B, T, cfg.num_q_heads, cfg.head_dim), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, T, cfg.num_q_heads), dtype=torch.float32, device="cuda")
+    ws = torch.empty(kv4.workspace_bytes(wl.layout, B * T, wl.alloc.page_table.shape[1]),
+                     dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def call():
+        kv4.decode_mq(wl.cache, wl.batch, q, T, out, lse, ws)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / steps * 1e3
+    extra = (T - 1) * B * cfg.num_q_heads * (cfg.head_dim * 4 + 4)
+    nbytes = decode_bytes + extra
+    del q, out, lse, ws
+    torch.cuda.empty_cache()
+    return {"T": T, "us": us, "query_tokens_per_s": B * T / (us * 1e-6),
+            "hbm_frac": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, "algorithmic_bytes": int(nbytes),
+            "vs_T_single_token_decodes": us / (T * decode_us),
+            "note": "plan + attend + merge; each query reads the cache itself"}
+
+
 def cpu_baseline(wl, budget_s=12.0, max_seqs=256):
     """The oracle, untuned, on a bounded sample of the same workload."""
     sys.path.insert(0, os.path.join(ROOT, "tests"))
@@ -331,6 +374,9 @@ def main():
     ap.add_argument("--config", type=int, default=CFG_IDX, choices=(2, 3),
                     help="2: one Qwen3-8B-shaped layer, B=1024 (the default line); 3: the 36-layer "
                          "decode step at B=512 (about 226 GB resident)")
+    ap.add_argument("--mq", type=int, default=0, metavar="T",
+                    help="also time the multi-query decode with T query tokens per sequence over "
+                         "the same cache (kv4_decode_attention_mq)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy 3 times (scales the HBM byte counters)")
     args = ap.parse_args()
@@ -405,6 +451,8 @@ def main():
             del w2
             torch.cuda.empty_cache()
         result["variants"] = var
+    if args.mq > 0:
+        result["multi_query"] = time_multi_query(wl, args.mq, max(10, args.steps // 2), 3, abytes, us["decode"])
     if not args.no_cpu:
         print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(wl)
