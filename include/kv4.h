@@ -271,10 +271,13 @@ kv4_status kvbf16_decode_phases(const kv4_layout* layout, const kv4_cache* cache
  *   lse    fp32 [batch][T][num_q_heads], or NULL
  * Queries with n <= 0 (T > N) give out = 0 and lse = -inf.  The workspace
  * is kv4_decode_workspace_size(layout, batch * T, max_pages); the 2^31-unit
- * bound of kv4_decode_attention applies to batch * T sequences.  Each query
- * reads the cache on its own (T reads of the shared positions; queries of
- * one sequence are scheduled next to each other so that the repeats are
- * served from the caches). */
+ * bound of kv4_decode_attention applies to batch * T sequences.  With INT4
+ * pages at head_dim 128 one work unit serves 16 / G queries of a kv head
+ * (G = num_q_heads / num_kv_heads; the MFMA columns are (query, head) pairs),
+ * so a block of queries reads and converts its K/V once; otherwise (kv8,
+ * kvbf16, head_dim 64, KV4_LAYOUT_INT8_QUERY) each query reads the cache on
+ * its own, next to the other queries of its sequence so that the repeats are
+ * served from the caches. */
 #define KV4_MAX_QUERIES 64
 kv4_status kv4_decode_attention_mq(const kv4_layout* layout, const kv4_cache* cache,
                                    const kv4_batch* batch, const uint16_t* q,

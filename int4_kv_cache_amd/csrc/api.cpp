@@ -132,6 +132,7 @@ kv4_status decode_impl(int fmt, const kv4_layout* L, const kv4_cache* c, const k
   p.slot_ids = b->slot_ids;
   p.batch = b->batch;
   p.nq = nq;
+  p.tq = 1;  // set by the launcher for the kernel it picks
   p.q = q;
   p.softmax_scale = sm;
   p.out = out;

@@ -591,14 +591,23 @@ __device__ inline int side_rows(int L, int N, int S, int R) {
   return L > g.rb ? S + nring : g.se;
 }
 
-// Work index v = b * nq + t: query t of sequence b sits at position N - nq + t
-// and sees positions [0, N - nq + t + 1).
-__device__ inline SeqWork seq_work(const DecodeParams& p, int v) {
+// Work blocks: query t of sequence b sits at position N - nq + t and sees
+// positions [0, N - nq + t + 1).  Block u = b * nqb + j holds the queries
+// [j * tq, min((j + 1) * tq, nq)) of sequence b and covers what its last
+// query sees.
+__device__ inline int n_blocks(const DecodeParams& p) { return (p.nq + p.tq - 1) / p.tq; }
+__device__ inline int block_queries(const DecodeParams& p, int u) {
+  const int t0 = (u % n_blocks(p)) * p.tq;
+  return p.nq - t0 < p.tq ? p.nq - t0 : p.tq;
+}
+
+__device__ inline SeqWork seq_work(const DecodeParams& p, int u) {
   SeqWork w;
-  const int b = v / p.nq, t = v - b * p.nq;
+  const int nqb = n_blocks(p);
+  const int b = u / nqb, t_last = (u % nqb) * p.tq + block_queries(p, u) - 1;
   int N = p.seq_lens[b];
   N = N < 0 ? 0 : (N > p.max_pages * kPage ? p.max_pages * kPage : N);
-  int L = N - p.nq + 1 + t;
+  int L = N - p.nq + 1 + t_last;
   L = L < 0 ? 0 : L;
   w.L = L;
   w.N = N;
@@ -620,11 +629,13 @@ __device__ inline int item_pages(const SeqWork& w, int chunk, int k) {
 }
 
 // Work-item descriptor, two int4:
-//   [0] = {v, L, first middle page of the item, (chunk index << 8) | pages}
-//   [1] = {items of v, first partial slot of v, side slot, N}
+//   [0] = {u, L, first middle page of the item, (chunk index << 8) | pages}
+//   [1] = {items of u, first partial slot of u, side slot, N}
+// Query j of a split block u keeps its partial of item k in slot
+// pbase + j * items + k.
 __device__ inline void write_item(const DecodeParams& p, uint32_t pos, int v, const SeqWork& w, int chunk, int k,
                                   int n, int pbase) {
-  const int b = v / p.nq;
+  const int b = v / n_blocks(p);
   const int slot = p.slot_ids ? p.slot_ids[b] : b;
   p.ws.items[2 * pos] = make_int4(v, w.L, w.mid_first + k * chunk, (k << 8) | item_pages(w, chunk, k));
   p.ws.items[2 * pos + 1] = make_int4(n, pbase, slot, w.N);
@@ -671,7 +682,7 @@ __global__ __launch_bounds__(1024) void worklist_kernel(DecodeParams p, int unit
   __shared__ uint32_t bucket[kMaxChunkPages + 2];
   __shared__ uint32_t nmerge;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
-  const int nv = p.batch * p.nq;  // work indices b * nq + t
+  const int nv = p.batch * n_blocks(p);  // work blocks
   for (int i = tid; i < kMaxChunkPages + 2; i += 1024) bucket[i] = 0u;
   if (tid == 0) nmerge = 0u;
   SeqWork w0{};
@@ -702,7 +713,7 @@ __global__ __launch_bounds__(1024) void worklist_kernel(DecodeParams p, int unit
         if (pg == chunk) ++full;
         else atomicAdd(&bucket[kMaxChunkPages - pg], 1u);
       }
-      split = n > 1 ? n : 0;
+      split = n > 1 ? n * block_queries(p, b) : 0;
     }
     unsigned long long tile = 0ull;
     const unsigned long long ex =
@@ -826,7 +837,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KV4_WAVES_P
     bool sh = false;
     if (lane < d.npg) {
       const int col = d.first + lane;
-      const int64_t x = p.page_table[int64_t(d.b / p.nq) * p.max_pages + col];
+      const int64_t x = p.page_table[int64_t(d.b / p.nq) * p.max_pages + col];  // tq = 1: u = b * nq + t
       v = (x < 0 || x >= p.num_pages) ? -1 : int(x);
       if constexpr (KV4 && KV4_NT_LOADS) {
         // the neighbouring work indices: other queries of this sequence or
@@ -1041,6 +1052,417 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KV4_WAVES_P
   }
 }
 
+// ------------------------------------------------ multi-query attention --
+// Several query tokens of one sequence read the same K/V.  A unit is
+// (item, kv head) and its 16 MFMA columns are (query, q head) pairs: 16 / G
+// queries of the G = Hq / Hkv heads of the kv head.  QK rows are positions and
+// every column uses every channel, so no MFMA work is wasted; the INT4 scales
+// are per (position, 32-channel group), so each group has its own QK
+// accumulator and its own P x V-scale operand.  INT4 pages and the INT8 side
+// tiles at head_dim 128.  Queries see different position ranges (query t of
+// T sees [0, N - T + t + 1)), so masks are per lane (column).
+
+template <bool NT>
+__device__ inline uint32_t ld4(const TileSrc& t, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(t.r, off, 0, NT ? 2 : 0);
+}
+
+// Per-lane byte offsets inside a block, D = 128, lane (ln = L % 16, kg = L / 16).
+struct McOff {
+  uint32_t k4, v4, s4, k8, v8, s8;
+  __device__ inline McOff(int ln, int kg) {
+    k4 = ln * 64 + kg * 4;               // INT4 K: + 16g -> channels 32g + 8kg .. +7 of row ln
+    v4 = 8 * 128 + (kg * 16 + ln) * 16;  // INT4 V: as the single-query tile
+    s4 = 16 * 128 + kg * 8;              // INT4 K scales of rows 4kg..4kg+3: + 32g; V scales + 128
+    k8 = ln * 128 + kg * 8;              // INT8 K: + 32g -> channels 32g + 8kg .. +7 of row ln
+    v8 = 16 * 128 + (kg * 16 + ln) * 32; // INT8 V: as the single-query tile
+    s8 = 32 * 128 + kg * 8;              // INT8 K scales of rows 4kg..4kg+3; V scales + 32
+  }
+};
+
+template <int KIND>
+struct McTile;
+
+template <>
+struct McTile<kInt4Page> {
+  static constexpr int kBytes = int(int4_block_bytes(128));
+  uint32_t k[4];      // group g: channels 32g + 8kg .. +7 of row ln (8 nibbles)
+  uint32_t v[4];      // V codes, the single-query tile's layout
+  uint32_t ks[4][2];  // group g: fp16 K scales of rows 4kg..4kg+3
+  uint32_t vs[4][2];
+  __device__ inline void load(const TileSrc& s, const McOff& o) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) k[g] = ld4<false>(s, o.k4 + 16 * g);
+    const uint4 a = ld16<false>(s, o.v4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const uint2 x = ld8<false>(s, o.s4 + 32 * g), y = ld8<false>(s, o.s4 + 128 + 32 * g);
+      ks[g][0] = x.x; ks[g][1] = x.y;
+      vs[g][0] = y.x; vs[g][1] = y.y;
+    }
+  }
+};
+
+template <>
+struct McTile<kInt8Tile> {
+  static constexpr int kBytes = int(int8_tile_bytes(128));
+  uint32_t k[8];  // group g: dwords 2g, 2g+1 = channels 32g + 8kg .. +7 of row ln
+  uint32_t v[8];
+  uint32_t ks[2], vs[2];  // one fp16 scale per row, rows 4kg..4kg+3
+  __device__ inline void load(const TileSrc& s, const McOff& o) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const uint2 a = ld8<false>(s, o.k8 + 32 * g);
+      k[2 * g] = a.x; k[2 * g + 1] = a.y;
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const uint4 b = ld16<false>(s, o.v8 + 16 * i);
+      v[4 * i] = b.x; v[4 * i + 1] = b.y; v[4 * i + 2] = b.z; v[4 * i + 3] = b.w;
+    }
+    const uint2 x = ld8<false>(s, o.s8), y = ld8<false>(s, o.s8 + 32);
+    ks[0] = x.x; ks[1] = x.y;
+    vs[0] = y.x; vs[1] = y.y;
+  }
+};
+
+struct McUnit {
+  bf16x8_t bq[4];  // group g: q of this lane's column, channels 32g + 8kg + (0 4 1 5 2 6 3 7)
+  float qs[4];     // group g: sum of the column's q over the group's 32 channels
+  f32x4_t o[8];    // PV accumulators: N-tile t, rows (columns) 4kg'..4kg'+3 of lane (n, kg')
+  f32x4_t corr[4]; // INT4 V-encoding correction per group, same layout
+  float m;         // running max (log2 units) of this lane's column
+  float l;         // this lane's share of the column's softmax denominator
+  float qk_scale;
+};
+
+// fp16 half e % 2 of word w[e / 2]
+__device__ inline float h2f_at(const uint32_t (&w)[2], int e) { return (e & 1) ? h2f_hi(w[e >> 1]) : h2f_lo(w[e >> 1]); }
+
+template <int KIND>
+__device__ inline void qk_mc(const McUnit& u, const McTile<KIND>& T, float (&x)[4]) {
+  if constexpr (KIND == kInt4Page) {
+    f32x4_t acc[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const float c = -kEncConst * u.qs[g];
+      const uint32_t d = T.k[g];
+      acc[g] = mfma(bf8(nib_pair<0>(d), nib_pair<1>(d), nib_pair<2>(d), nib_pair<3>(d)), u.bq[g],
+                    f32x4_t{c, c, c, c});
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float s = acc[0][e] * h2f_at(T.ks[0], e);
+      s = fmaf(acc[1][e], h2f_at(T.ks[1], e), s);
+      s = fmaf(acc[2][e], h2f_at(T.ks[2], e), s);
+      x[e] = fmaf(acc[3][e], h2f_at(T.ks[3], e), s);
+    }
+  } else {
+    f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const uint32_t w0 = T.k[2 * g], w1 = T.k[2 * g + 1];
+      acc = mfma(bf8(pack_exact(sbyte(w0, 0), sbyte(w1, 0)), pack_exact(sbyte(w0, 1), sbyte(w1, 1)),
+                     pack_exact(sbyte(w0, 2), sbyte(w1, 2)), pack_exact(sbyte(w0, 3), sbyte(w1, 3))),
+                 u.bq[g], acc);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] = acc[e] * h2f_at(T.ks, e);
+  }
+}
+
+// p (8 positions: rows 4kg..4kg+3 of T0 then of T1) times a per-position
+// factor, split into bf16 hi + lo A operands
+__device__ inline void split_a(const float (&ap)[8], bf16x8_t& a_hi, bf16x8_t& a_lo) {
+  uint32_t hi[4], lo[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    hi[j] = pack_bf16(ap[2 * j], ap[2 * j + 1]);
+    const float h0 = __uint_as_float(__builtin_amdgcn_perm(0u, hi[j], 0x01000c0cu));
+    lo[j] = pack_bf16(ap[2 * j] - h0, ap[2 * j + 1] - bf16_hi(hi[j]));
+  }
+  a_hi = bf8(hi[0], hi[1], hi[2], hi[3]);
+  a_lo = bf8(lo[0], lo[1], lo[2], lo[3]);
+}
+
+// One step of two tiles.  va0 / va1: this lane's valid rows (4 bits) of each tile.
+template <int KIND>
+__device__ inline void step_mc(McUnit& u, const McTile<KIND>& T0, const McTile<KIND>& T1, uint32_t va0,
+                               uint32_t va1, int lane) {
+  float x0[4], x1[4];
+  qk_mc<KIND>(u, T0, x0);
+  qk_mc<KIND>(u, T1, x1);
+  if (!__all((va0 & va1) == 15u)) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x0[e] = ((va0 >> e) & 1u) ? x0[e] : -INFINITY;
+      x1[e] = ((va1 >> e) & 1u) ? x1[e] : -INFINITY;
+    }
+  }
+  float mx = max3(max3(x0[0], x0[1], x0[2]), max3(x0[3], x1[0], x1[1]), max3(x1[2], x1[3], -INFINITY));
+  const float sc = KIND == kInt4Page ? kEnc * u.qk_scale : u.qk_scale;
+  // lazy running max of a column, as in the single-query step
+  if (__any(mx * sc > u.m + kRescale)) {
+    mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+    const float mn = fmaxf(u.m, mx * sc);
+    const float alpha = (mn == u.m) ? 1.0f : __builtin_amdgcn_exp2f(u.m - mn);
+    u.l *= alpha;
+    u.m = mn;
+    // accumulator row e of lane (n, kg') is column 4kg' + e, held by lane 4kg' + e
+    const int c0 = 4 * (lane >> 4);
+    const f32x4_t f = {__shfl(alpha, c0, kWave), __shfl(alpha, c0 + 1, kWave), __shfl(alpha, c0 + 2, kWave),
+                       __shfl(alpha, c0 + 3, kWave)};
+#pragma unroll
+    for (int t = 0; t < 8; ++t) u.o[t] *= f;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) u.corr[g] *= f;
+  }
+  const float mneg = u.m == -INFINITY ? 0.0f : -u.m;
+  float pr[8];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    pr[e] = __builtin_amdgcn_exp2f(fmaf(x0[e], sc, mneg));
+    pr[e + 4] = __builtin_amdgcn_exp2f(fmaf(x1[e], sc, mneg));
+  }
+  u.l += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
+
+  if constexpr (KIND == kInt4Page) {
+    constexpr uint32_t kNeg = (0xBF80u | (8u << kEncShift)) * 0x00010001u;
+    const bf16x8_t ones = bf8(kNeg, kNeg, kNeg, kNeg);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      float ap[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        ap[e] = pr[e] * h2f_at(T0.vs[g], e);
+        ap[e + 4] = pr[e + 4] * h2f_at(T1.vs[g], e);
+      }
+      bf16x8_t a_hi, a_lo;
+      split_a(ap, a_hi, a_lo);
+      u.corr[g] = mfma(a_hi, ones, u.corr[g]);
+      u.corr[g] = mfma(a_lo, ones, u.corr[g]);
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const int t = 2 * g + tt, j = t & 3, w = t >> 2;
+        const bf16x8_t bv = bf8(nib_pair_at(T0.v[w], j), nib_pair_at(T0.v[2 + w], j), nib_pair_at(T1.v[w], j),
+                                nib_pair_at(T1.v[2 + w], j));
+        f32x4_t c = u.o[t];
+        c = mfma(a_hi, bv, c);
+        c = mfma(a_lo, bv, c);
+        u.o[t] = c;
+      }
+    }
+  } else {
+    float ap[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      ap[e] = pr[e] * h2f_at(T0.vs, e) * (1.0f / kEnc);
+      ap[e + 4] = pr[e + 4] * h2f_at(T1.vs, e) * (1.0f / kEnc);
+    }
+    bf16x8_t a_hi, a_lo;
+    split_a(ap, a_hi, a_lo);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const uint32_t a = T0.v[t], b = T1.v[t];
+      const bf16x8_t bv = bf8(pack_exact(sbyte(a, 0), sbyte(a, 1)), pack_exact(sbyte(a, 2), sbyte(a, 3)),
+                              pack_exact(sbyte(b, 0), sbyte(b, 1)), pack_exact(sbyte(b, 2), sbyte(b, 3)));
+      f32x4_t c = u.o[t];
+      c = mfma(a_hi, bv, c);
+      c = mfma(a_lo, bv, c);
+      u.o[t] = c;
+    }
+  }
+}
+
+// n tiles two at a time, two-stage register pipeline; loads past the end get
+// an empty range (zeros), as in run_tiles.  mask(i) -> this lane's valid rows.
+template <int KIND, class PtrFn, class MaskFn, class SetupFn>
+__device__ inline void run_mc(McUnit& u, int n, PtrFn ptr, MaskFn mask, int lane, SetupFn setup) {
+  if (n <= 0) return;
+  const McOff off(lane & 15, lane >> 4);
+  const int nsteps = (n + 1) >> 1;
+  const int last = nsteps - 1;
+  constexpr int kBytes = McTile<KIND>::kBytes;
+  auto load = [&](McTile<KIND>& t0, McTile<KIND>& t1, int s) {
+    const bool live = s <= last;
+    s = s < last ? s : last;
+    const int i = 2 * s;
+    t0.load(TileSrc(ptr(i), live ? kBytes : 0), off);
+    t1.load(TileSrc(ptr(i + 1 < n ? i + 1 : i), live && i + 1 < n ? kBytes : 0), off);
+  };
+  auto run = [&](const McTile<KIND>& t0, const McTile<KIND>& t1, int s) {
+    const int i = 2 * s;
+    step_mc<KIND>(u, t0, t1, mask(i), i + 1 < n ? mask(i + 1) : 0u, lane);
+  };
+  McTile<KIND> a0, a1, b0, b1;
+  load(a0, a1, 0);
+  setup();
+  for (int s = 0;; s += 2) {
+    load(b0, b1, s + 1);
+    run(a0, a1, s);
+    if (s + 1 >= nsteps) break;
+    load(a0, a1, s + 2);
+    run(b0, b1, s + 1);
+    if (s + 2 >= nsteps) break;
+  }
+}
+
+// rows [lo, hi) of a 4-row run starting at row r: bits 0..3
+__device__ inline uint32_t rows4(int r, int lo, int hi) {
+  lo = lo - r;
+  hi = hi - r;
+  lo = lo < 0 ? 0 : lo;
+  hi = hi > 4 ? 4 : hi;
+  return hi > lo ? ((1u << hi) - 1u) & ~((1u << lo) - 1u) : 0u;
+}
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KV4_WAVES_PER_EU, 8))) void attention_mc_kernel(
+    DecodeParams p) {
+  constexpr int D = 128, NT = 8;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int ln = lane & 15, kg = lane >> 4;
+  const int H = p.num_kv_heads, Hq = p.num_q_heads, G = Hq / H;
+  const int S = p.n_sink, R = p.n_recent;
+  const int T = p.nq, nqb = n_blocks(p);
+  const uint32_t units = p.ws.header[1] * uint32_t(H);
+  if (units == 0) return;
+  const uint32_t nw = gridDim.x * (blockDim.x / kWave);
+  for (uint32_t t0 = blockIdx.x * (blockDim.x / kWave) + uniform(threadIdx.x / kWave); t0 < units; t0 += nw) {
+    const ItemDesc d = decode_item(load_item(p, t0 / uint32_t(H)));
+    const int h = int(t0 % uint32_t(H));
+    const int bseq = d.b / nqb, tb = (d.b % nqb) * p.tq;  // sequence, first query of the block
+    const int nqs = T - tb < p.tq ? T - tb : p.tq;        // queries in the block
+    const int N = d.N;
+    const Regions g = regions_in(d.L, N, S, R);  // the block's union (its last query)
+
+    // ---- this lane's QK column: query tb + ln / G, head ln % G
+    const int qj = ln / G, hj = ln % G;
+    const bool col_ok = qj < nqs;
+    const int ncol = col_ok ? N - T + tb + qj + 1 : 0;  // positions the column sees: [0, ncol)
+
+    McUnit u;
+    uint4 qraw[4];
+    bool pending = true;
+    {
+      const uint16_t* qrow = p.q + ((int64_t(bseq) * T + tb + (col_ok ? qj : 0)) * Hq + h * G + hj) * D;
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg) {
+        qraw[gg] = make_uint4(0u, 0u, 0u, 0u);
+        if (col_ok) qraw[gg] = *reinterpret_cast<const uint4*>(qrow + 32 * gg + 8 * kg);
+      }
+#pragma unroll
+      for (int t = 0; t < NT; ++t) u.o[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg) u.corr[gg] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      u.m = -INFINITY;
+      u.l = 0.f;
+      u.qk_scale = p.softmax_scale * kLog2e;
+    }
+    auto setup = [&]() {
+      if (!pending) return;
+      pending = false;
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg) {
+        const uint32_t w0 = qraw[gg].x, w1 = qraw[gg].y, w2 = qraw[gg].z, w3 = qraw[gg].w;
+        u.bq[gg] = bf8(__builtin_amdgcn_perm(w2, w0, 0x05040100u), __builtin_amdgcn_perm(w2, w0, 0x07060302u),
+                       __builtin_amdgcn_perm(w3, w1, 0x05040100u), __builtin_amdgcn_perm(w3, w1, 0x07060302u));
+        float qs = ((bf16_lo(w0) + bf16_hi(w0)) + (bf16_lo(w1) + bf16_hi(w1))) +
+                   ((bf16_lo(w2) + bf16_hi(w2)) + (bf16_lo(w3) + bf16_hi(w3)));
+        qs += __shfl_xor(qs, 16, kWave);
+        qs += __shfl_xor(qs, 32, kWave);
+        u.qs[gg] = qs;
+      }
+    };
+
+    // ---- protected rows: INT8 side tiles of the first item
+    if (d.ck == 0 && d.L > 0 && S + R > 0 && d.slot >= 0 && d.slot < p.num_slots) {
+      const int nring = N > S ? (N - S < R ? N - S : R) : 0;
+      const int ring0 = N - R > S ? N - R : S;
+      const int rows = d.L > g.rb ? S + nring : g.se;
+      const int ntiles = (rows + kPage - 1) / kPage;
+      const int shift = R > 0 ? (ring0 - S) % R : 0;  // ring row of position ring0
+      const int sink_end = ncol < S ? ncol : S;
+      const uint8_t* sblk = p.side + (int64_t(d.slot) * H + h) * p.side_bytes;
+      auto ptr = [&](int i) { return sblk + int64_t(i) * int8_tile_bytes(D); };
+      auto mask = [&](int i) {
+        uint32_t v = 0u;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int rho = i * kPage + 4 * kg + e;
+          bool ok;
+          if (rho < S) {
+            ok = rho < sink_end;
+          } else {
+            const int r = rho - S;
+            const int pos = ring0 + (r - shift + R) % (R > 0 ? R : 1);
+            ok = r < nring && pos < ncol;
+          }
+          v |= ok ? (1u << e) : 0u;
+        }
+        return v;
+      };
+      run_mc<kInt8Tile>(u, ntiles, ptr, mask, lane, setup);
+    }
+
+    // ---- middle pages of the item
+    if (d.npg > 0) {
+      int pid0 = 0;
+      if (lane < d.npg) {
+        const int64_t x = p.page_table[int64_t(bseq) * p.max_pages + d.first + lane];
+        pid0 = (x < 0 || x >= p.num_pages) ? -1 : int(x);
+      }
+      auto ptr = [&](int i) {
+        const int pid = __builtin_amdgcn_readlane(pid0, i);
+        return p.pages + (int64_t(pid < 0 ? 0 : pid) * H + h) * p.block_bytes;
+      };
+      const int me = g.me < ncol ? g.me : ncol;  // this column's end of the INT4 region
+      auto mask = [&](int i) {
+        const int pid = __builtin_amdgcn_readlane(pid0, i);
+        return pid < 0 ? 0u : rows4((d.first + i) * kPage + 4 * kg, g.mb, me);
+      };
+      run_mc<kInt4Page>(u, d.npg, ptr, mask, lane, setup);
+    }
+
+    // ---- finish: the column's denominator, then outputs or partials
+    float lt = u.l;
+    lt += __shfl_xor(lt, 16, kWave);
+    lt += __shfl_xor(lt, 32, kWave);
+    const int64_t pbase = d.pbase;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int col = 4 * kg + e;  // accumulator row e of this lane
+      const float lh = __shfl(lt, col, kWave);
+      const int cq = col / G, chj = col % G;
+      if (cq < nqs) {
+        const int64_t row = (int64_t(bseq) * T + tb + cq) * Hq + h * G + chj;
+        const int64_t slot = pbase + int64_t(cq) * d.nitems + d.ck;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          const float o = u.o[t][e] + u.corr[t >> 1][e];
+          const int c = 16 * t + ln;
+          if (d.nitems == 1) {
+            p.out[row * D + c] = f32_to_bf16_bits(lh > 0.f ? kEnc * o / lh : 0.f);
+          } else {
+            p.ws.partials[(slot * Hq + h * G + chj) * (D + 2) + c] = kEnc * o;
+          }
+        }
+      }
+    }
+    if (kg == 0 && col_ok) {
+      const int64_t row = (int64_t(bseq) * T + tb + qj) * Hq + h * G + hj;
+      if (d.nitems == 1) {
+        if (p.lse) p.lse[row] = lt > 0.f ? (u.m + log2f(lt)) * kLn2 : -INFINITY;
+      } else {
+        float* part = p.ws.partials + ((pbase + int64_t(qj) * d.nitems + d.ck) * Hq + h * G + hj) * (D + 2);
+        part[D] = u.m;
+        part[D + 1] = lt;
+      }
+    }
+  }
+}
+
 // ----------------------------------------------------------------- merge ---
 // Exact log-sum-exp merge of the partials of split sequences ([NEWS]
 // Interpretation para 3); a persistent grid strides over (split sequence,
@@ -1054,11 +1476,16 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeParams p) {
   const int lane = threadIdx.x & (kWave - 1);
   const int Hq = p.num_q_heads;
   const int64_t nw = int64_t(gridDim.x) * (blockDim.x / kWave);
-  const int64_t tasks = int64_t(p.ws.header[3]) * Hq;
+  const int nqb = n_blocks(p);
+  const int64_t per = int64_t(p.tq) * Hq;  // (query of the block, head) pairs
+  const int64_t tasks = int64_t(p.ws.header[3]) * per;
   for (int64_t w = int64_t(blockIdx.x) * (blockDim.x / kWave) + threadIdx.x / kWave; w < tasks; w += nw) {
-    const int b = p.ws.merge_list[w / Hq], hq = int(w % Hq);
-    const int n = p.ws.item_count[b];
-    const float* base = p.ws.partials + (int64_t(p.ws.item_base[b]) * Hq + hq) * (D + 2);
+    const int u = p.ws.merge_list[w / per];
+    const int j = int((w % per) / Hq), hq = int(w % Hq);
+    if (j >= block_queries(p, u)) continue;
+    const int b = (u / nqb) * p.nq + (u % nqb) * p.tq + j;  // output row: query t of sequence b
+    const int n = p.ws.item_count[u];
+    const float* base = p.ws.partials + ((int64_t(p.ws.item_base[u]) + int64_t(j) * n) * Hq + hq) * (D + 2);
     const int64_t stride = int64_t(Hq) * (D + 2);
     float M = -INFINITY, l = 0.f, o[E];
 #pragma unroll
@@ -1125,18 +1552,26 @@ hipError_t launch_fd(DecodeParams p, unsigned phases, hipStream_t stream) {
   constexpr int HB = 16 / (D / 32);
   const int cus = device_cus();
   if (cus <= 0) return hipErrorInvalidDevice;
+  const int G = p.num_q_heads / p.num_kv_heads;
+  // several queries per sequence on INT4 pages at head_dim 128: one unit
+  // holds 16 / G queries of the kv head's G heads
+  const bool mc = FMT == kFmtKV4 && D == 128 && p.nq > 1 && G <= 16 && 16 % G == 0;
+  p.tq = mc ? 16 / G : 1;
   // the work list is sized for the attention grid, so both use the same count
-  const int blocks = cus * blocks_per_cu(attention_kernel<FMT, D>);
+  const int blocks = cus * (mc ? blocks_per_cu(attention_mc_kernel) : blocks_per_cu(attention_kernel<FMT, D>));
   p.resident_waves = blocks * 4;
   if (phases & 1u) {
-    const int G = p.num_q_heads / p.num_kv_heads;
-    const int units_per_item = p.num_kv_heads * ((G + HB - 1) / HB);
+    const int units_per_item = mc ? p.num_kv_heads : p.num_kv_heads * ((G + HB - 1) / HB);
     hipLaunchKernelGGL(worklist_kernel, dim3(1), dim3(1024), 0, stream, p, units_per_item);
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
   if (phases & 2u) {
-    hipLaunchKernelGGL((attention_kernel<FMT, D>), dim3(blocks), dim3(256), 0, stream, p);
+    if (mc) {
+      hipLaunchKernelGGL(attention_mc_kernel, dim3(blocks), dim3(256), 0, stream, p);
+    } else {
+      hipLaunchKernelGGL((attention_kernel<FMT, D>), dim3(blocks), dim3(256), 0, stream, p);
+    }
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }

@@ -52,7 +52,8 @@ struct DecodeParams {
   const int32_t* seq_lens;
   const int32_t* slot_ids;
   int32_t batch;
-  int32_t nq;  // query tokens per sequence (the last nq positions); work is indexed by b * nq + t
+  int32_t nq;  // query tokens per sequence (the last nq positions)
+  int32_t tq;  // queries per work block: work index u = b * ceil(nq / tq) + t / tq
   const uint16_t* q;
   float softmax_scale;
   uint16_t* out;

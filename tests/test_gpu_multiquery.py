@@ -86,6 +86,37 @@ def test_multiquery_qwen_shapes(kv4, T):
     _check(kv4, wl, T, "qwen shapes")
 
 
+@pytest.mark.parametrize("T", [3, 5, 6, 12])
+def test_multiquery_blocks_and_short_ring(kv4, T):
+    """Qwen shapes with a ring of 8: blocks of four queries, partial last
+    blocks, and queries whose view ends inside the INT4 region."""
+    from harness import build_from_host
+
+    lengths = np.array([1500, 333, 40, 12, 700], dtype=np.int32)
+    wl = build_from_host(1, 0, lengths=lengths, n_sink=16, n_recent=8)
+    _check(kv4, wl, T, "qwen shapes S=16 R=8")
+
+
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (16, 8), (8, 1), (4, 1)])
+def test_multiquery_group_sizes(kv4, hq, hkv):
+    """Head dim 128 with 1, 2, 8 and 4 query heads per kv head (16, 8, 2 and
+    4 queries per block; the layout allows up to 8 per kv head)."""
+    import dataclasses
+
+    import workloads.configs as wc
+    from harness import build_from_host
+
+    base = wc.CONFIGS[1]
+    cfg = dataclasses.replace(base, idx=91, name=f"mq-shape-{hq}-{hkv}", num_q_heads=hq, num_kv_heads=hkv)
+    wc.CONFIGS[91] = cfg
+    try:
+        wl = build_from_host(91, 0, lengths=np.array([1, 160, 1300, 77], dtype=np.int32))
+        for T in (3, 17):
+            _check(kv4, wl, T, f"hq={hq} hkv={hkv}")
+    finally:
+        del wc.CONFIGS[91]
+
+
 def test_multiquery_rejects_bad_counts(kv4):
     import torch
 
