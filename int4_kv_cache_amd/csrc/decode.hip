@@ -48,6 +48,9 @@ typedef uint32_t u32x4_t __attribute__((__vector_size__(16)));
 #ifndef KV4_STAGES
 #define KV4_STAGES 3  // pipeline depth of the INT4 page loop
 #endif
+#ifndef KV4_MC_STAGES
+#define KV4_MC_STAGES 1  // pipeline depth of the multi-column kernel (2 measured 1.3% slower)
+#endif
 #ifndef KV4_STAGES8
 #define KV4_STAGES8 2  // pipeline depth of the INT8 tile loops
 #endif
@@ -1137,7 +1140,10 @@ struct McUnit {
   float qk_scale;
 };
 
-// fp16 half e % 2 of word w[e / 2]
+// x times fp16 half e % 2 of word w[e / 2], as one mixed-precision FMA
+__device__ inline float mul_h_at(float x, const uint32_t (&w)[2], int e) {
+  return (e & 1) ? mul_h_hi(x, w[e >> 1]) : mul_h_lo(x, w[e >> 1]);
+}
 __device__ inline float h2f_at(const uint32_t (&w)[2], int e) { return (e & 1) ? h2f_hi(w[e >> 1]) : h2f_lo(w[e >> 1]); }
 
 template <int KIND>
@@ -1153,7 +1159,7 @@ __device__ inline void qk_mc(const McUnit& u, const McTile<KIND>& T, float (&x)[
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      float s = acc[0][e] * h2f_at(T.ks[0], e);
+      float s = mul_h_at(acc[0][e], T.ks[0], e);
       s = fmaf(acc[1][e], h2f_at(T.ks[1], e), s);
       s = fmaf(acc[2][e], h2f_at(T.ks[2], e), s);
       x[e] = fmaf(acc[3][e], h2f_at(T.ks[3], e), s);
@@ -1168,7 +1174,7 @@ __device__ inline void qk_mc(const McUnit& u, const McTile<KIND>& T, float (&x)[
                  u.bq[g], acc);
     }
 #pragma unroll
-    for (int e = 0; e < 4; ++e) x[e] = acc[e] * h2f_at(T.ks, e);
+    for (int e = 0; e < 4; ++e) x[e] = mul_h_at(acc[e], T.ks, e);
   }
 }
 
@@ -1236,8 +1242,8 @@ __device__ inline void step_mc(McUnit& u, const McTile<KIND>& T0, const McTile<K
       float ap[8];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        ap[e] = pr[e] * h2f_at(T0.vs[g], e);
-        ap[e + 4] = pr[e + 4] * h2f_at(T1.vs[g], e);
+        ap[e] = mul_h_at(pr[e], T0.vs[g], e);
+        ap[e + 4] = mul_h_at(pr[e + 4], T1.vs[g], e);
       }
       bf16x8_t a_hi, a_lo;
       split_a(ap, a_hi, a_lo);
@@ -1258,8 +1264,8 @@ __device__ inline void step_mc(McUnit& u, const McTile<KIND>& T0, const McTile<K
     float ap[8];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      ap[e] = pr[e] * h2f_at(T0.vs, e) * (1.0f / kEnc);
-      ap[e + 4] = pr[e + 4] * h2f_at(T1.vs, e) * (1.0f / kEnc);
+      ap[e] = mul_h_at(pr[e] * (1.0f / kEnc), T0.vs, e);
+      ap[e + 4] = mul_h_at(pr[e + 4] * (1.0f / kEnc), T1.vs, e);
     }
     bf16x8_t a_hi, a_lo;
     split_a(ap, a_hi, a_lo);
@@ -1296,16 +1302,25 @@ __device__ inline void run_mc(McUnit& u, int n, PtrFn ptr, MaskFn mask, int lane
     const int i = 2 * s;
     step_mc<KIND>(u, t0, t1, mask(i), i + 1 < n ? mask(i + 1) : 0u, lane);
   };
-  McTile<KIND> a0, a1, b0, b1;
-  load(a0, a1, 0);
-  setup();
-  for (int s = 0;; s += 2) {
-    load(b0, b1, s + 1);
-    run(a0, a1, s);
-    if (s + 1 >= nsteps) break;
-    load(a0, a1, s + 2);
-    run(b0, b1, s + 1);
-    if (s + 2 >= nsteps) break;
+  if constexpr (KV4_MC_STAGES == 1) {
+    for (int s = 0; s < nsteps; ++s) {
+      McTile<KIND> a0, a1;
+      load(a0, a1, s);
+      setup();
+      run(a0, a1, s);
+    }
+  } else {
+    McTile<KIND> a0, a1, b0, b1;
+    load(a0, a1, 0);
+    setup();
+    for (int s = 0;; s += 2) {
+      load(b0, b1, s + 1);
+      run(a0, a1, s);
+      if (s + 1 >= nsteps) break;
+      load(a0, a1, s + 2);
+      run(b0, b1, s + 1);
+      if (s + 2 >= nsteps) break;
+    }
   }
 }
 
