@@ -206,6 +206,26 @@ def time_multi_query(wl, T, steps, warmup, decode_bytes, decode_us):
                     "queries (the multi-column kernel), otherwise each query reads the cache itself"}
 
 
+def capacity(budget_gb=240.0, layers=36, repeats=64):
+    """Concurrent sequences whose cache fits a fixed budget (kv4_cache_capacity,
+    host arithmetic): Qwen3-8B attention (36 layers, Hkv 8, D 128) with the
+    config-2 length distribution tiled `repeats` times.  240 GB is the MI355X's
+    288 GB less the bf16 weights (about 16 GB) and about 10% headroom."""
+    import int4_kv_cache_amd as kv4
+    from workloads import context_lengths, get_config
+
+    cfg = get_config(CFG_IDX)
+    lengths = np.tile(context_lengths(cfg), repeats)
+    budget = int(budget_gb * 1e9)
+    out = {}
+    for name, fmt, S, R in (("bf16", kv4.FMT_BF16, 0, 0), ("kv8", kv4.FMT_KV8, 0, 0),
+                            ("int4_plain", kv4.FMT_KV4, 0, 0), ("kv4_rl", kv4.FMT_KV4, cfg.n_sink, cfg.n_recent)):
+        lay = kv4.make_layout(cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim, S, R)
+        out[name] = kv4.cache_capacity(lay, fmt, layers, lengths, budget)[1]
+    return {"budget_gb": budget_gb, "layers": layers, "lengths": "config-2 distribution (mean %.0f)" % lengths.mean(),
+            "sequences": out, "vs_bf16": {k: out[k] / out["bf16"] for k in out}}
+
+
 def cpu_baseline(wl, budget_s=12.0, max_seqs=256):
     """The oracle, untuned, on a bounded sample of the same workload."""
     sys.path.insert(0, os.path.join(ROOT, "tests"))
@@ -430,6 +450,7 @@ def main():
                    "decode_hbm_frac": abytes / (us["decode"] * 1e-6) / 1e9 / HBM_PEAK_GBS,
                    "decode_algorithmic_bytes": abytes},
         "hbm_read_probe_gbs": read_probe_gbs(),
+        "capacity": capacity(),
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(),
                      "kernel": "attention_kernel<kv4, 128> (the ATTEND phase)",

@@ -295,6 +295,25 @@ kv4_status kvbf16_decode_attention_mq(const kv4_layout* layout, const kv4_cache*
                                       uint16_t* out, float* lse, void* workspace,
                                       size_t workspace_bytes, hipStream_t stream);
 
+/* ---- capacity model (host) ---------------------------------------------------
+ * The pages credit part of the end-to-end gain to the higher concurrency a
+ * smaller cache allows, and note that a fixed page budget limits it ([NEWS]
+ * Perspective paragraphs 1 and 2).  For `num_layers` layers of this layout in
+ * `format` (KV4_FORMAT_*), sequence i of `seq_lens` (host array of n lengths,
+ * each >= 0) holds ceil(seq_lens[i] / page_size) pages per layer, each of
+ * num_kv_heads blocks of *_block_bytes; with KV4_FORMAT_KV4 and
+ * n_sink + n_recent > 0 it also holds one side block of kv4_side_bytes per kv
+ * head and layer.  Writes *total_bytes, the bytes of all n sequences, and
+ * *fit, the largest k such that sequences 0 .. k-1 fit in budget_bytes.
+ * Host arithmetic only (no device call); KV4_ERR_INVALID_ARG for a negative
+ * length, n < 0, num_layers < 1 or an unknown format. */
+#define KV4_FORMAT_KV4 0
+#define KV4_FORMAT_KV8 1
+#define KV4_FORMAT_BF16 2
+kv4_status kv4_cache_capacity(const kv4_layout* layout, int32_t format, int32_t num_layers,
+                              const int32_t* seq_lens, int32_t n, uint64_t budget_bytes,
+                              uint64_t* total_bytes, int32_t* fit);
+
 /* ---- measurement aid ----------------------------------------------------------
  * Streams `bytes` (a multiple of 16) of `buf` through 128-bit nontemporal
  * loads, each wave reading its own contiguous share in whole-KiB pieces, and

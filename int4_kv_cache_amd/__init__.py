@@ -60,6 +60,7 @@ EXPORTS = [
     "kv4_decode_attention", "kv8_decode_attention", "kvbf16_decode_attention",
     "kv4_decode_phases", "kv8_decode_phases", "kvbf16_decode_phases",
     "kv4_decode_attention_mq", "kv8_decode_attention_mq", "kvbf16_decode_attention_mq",
+    "kv4_cache_capacity",
     "kv4_probe_blocks", "kv4_hbm_read_probe",
 ]
 
@@ -98,6 +99,9 @@ def load(path: Optional[str] = None):
         f.argtypes = [P, P, P, P, i32, ctypes.c_float, P, P, P, sz, P]
     L.kv4_decode_workspace_size.restype = ctypes.c_int
     L.kv4_decode_workspace_size.argtypes = [P, i32, i32, ctypes.POINTER(sz)]
+    L.kv4_cache_capacity.restype = ctypes.c_int
+    L.kv4_cache_capacity.argtypes = [P, i32, i32, P, i32, ctypes.c_uint64, ctypes.POINTER(ctypes.c_uint64),
+                                     ctypes.POINTER(i32)]
     L.kv4_probe_blocks.restype = i32
     L.kv4_probe_blocks.argtypes = []
     L.kv4_hbm_read_probe.restype = ctypes.c_int
@@ -211,6 +215,21 @@ def decode(cache: Cache, batch: Batch, q, out, lse, workspace, softmax_scale: fl
 
 
 MAX_QUERIES = 64
+
+
+def cache_capacity(layout: Layout, fmt: int, num_layers: int, seq_lens, budget_bytes: int):
+    """Host capacity model: (bytes of all sequences over num_layers layers,
+    number of leading sequences that fit in budget_bytes).  seq_lens: host ints."""
+    import numpy as np
+
+    sl = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    tot = ctypes.c_uint64(0)
+    fit = ctypes.c_int32(0)
+    st = load().kv4_cache_capacity(ctypes.byref(layout), int(fmt), int(num_layers),
+                                   ctypes.c_void_p(sl.ctypes.data) if sl.size else None, int(sl.size),
+                                   ctypes.c_uint64(int(budget_bytes)), ctypes.byref(tot), ctypes.byref(fit))
+    _check("kv4_cache_capacity", st)
+    return int(tot.value), int(fit.value)
 
 
 def decode_mq(cache: Cache, batch: Batch, q, num_queries: int, out, lse, workspace,

@@ -248,6 +248,30 @@ kv4_status kvbf16_decode_attention_mq(const kv4_layout* L, const kv4_cache* c, c
   return decode_impl(kFmtBF16, L, c, b, q, sm, out, lse, ws, ws_bytes, kAllPhases, stream, num_queries);
 }
 
+kv4_status kv4_cache_capacity(const kv4_layout* L, int32_t format, int32_t num_layers, const int32_t* seq_lens,
+                              int32_t n, uint64_t budget, uint64_t* total, int32_t* fit) {
+  if (!total || !fit || n < 0 || num_layers < 1 || (n > 0 && !seq_lens)) return KV4_ERR_INVALID_ARG;
+  if (format != KV4_FORMAT_KV4 && format != KV4_FORMAT_KV8 && format != KV4_FORMAT_BF16) return KV4_ERR_INVALID_ARG;
+  const int fmt = format == KV4_FORMAT_KV4 ? kFmtKV4 : (format == KV4_FORMAT_KV8 ? kFmtKV8 : kFmtBF16);
+  const kv4_status s = layout_check(L, fmt);
+  if (s != KV4_OK) return s;
+  const uint64_t per_page = uint64_t(L->num_kv_heads) * block_bytes(L, fmt) * uint64_t(num_layers);
+  const uint64_t per_seq = protected_set(L, fmt) ? uint64_t(L->num_kv_heads) * side_bytes(L) * uint64_t(num_layers) : 0;
+  uint64_t sum = 0;
+  int32_t k = 0;
+  bool full = false;
+  for (int32_t i = 0; i < n; ++i) {
+    if (seq_lens[i] < 0) return KV4_ERR_INVALID_ARG;
+    const uint64_t pages = (uint64_t(seq_lens[i]) + uint64_t(L->page_size) - 1) / uint64_t(L->page_size);
+    sum += pages * per_page + per_seq;
+    if (!full && sum <= budget) k = i + 1;
+    else full = true;
+  }
+  *total = sum;
+  *fit = k;
+  return KV4_OK;
+}
+
 int32_t kv4_probe_blocks(void) { return kv4::probe_blocks(); }
 
 kv4_status kv4_hbm_read_probe(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream) {

@@ -86,6 +86,8 @@ def lib():
         L.orc_decode_mq.argtypes = [ctypes.c_int, P, P, i64, P, i32, P, i32, P, P, i32, P, i32,
                                     ctypes.c_double, P, i32, P, P, P, i32]
         L.orc_decode_mq.restype = ctypes.c_int
+        L.orc_cache_capacity.argtypes = [ctypes.c_int, P, i32, P, i32, ctypes.c_uint64, P, P]
+        L.orc_cache_capacity.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -256,3 +258,15 @@ def decode_mq(cache: HostCache, page_table, seq_lens, slot_ids, q_bf16, num_quer
     if rc != 0:
         raise ValueError(f"oracle multi-query decode rejected its input (code {rc})")
     return out, lse, float(gap[0])
+
+
+def cache_capacity(fmt: int, lay: Layout, num_layers: int, seq_lens, budget: int):
+    """(bytes of all sequences, how many leading sequences fit in budget)."""
+    sl = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    tot = np.zeros(1, dtype=np.uint64)
+    fit = np.zeros(1, dtype=np.int32)
+    rc = lib().orc_cache_capacity(fmt, ctypes.byref(lay), int(num_layers), _ptr(sl), sl.size,
+                                  ctypes.c_uint64(int(budget)), _ptr(tot), _ptr(fit))
+    if rc != 0:
+        raise ValueError(f"oracle capacity rejected its input (code {rc})")
+    return int(tot[0]), int(fit[0])

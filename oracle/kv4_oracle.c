@@ -631,3 +631,31 @@ int orc_decode_mq(int fmt, const orc_layout* L, const uint8_t* pages,
   *max_gap = gap_all;
   return status;
 }
+
+/* Cache bytes of a batch and how many of its sequences fit in a budget
+ * ([NEWS] Perspective paragraphs 1 and 2: a smaller cache allows higher
+ * concurrency, and a fixed page budget limits it).  A sequence of length L
+ * holds ceil(L / page_size) pages per layer, each of num_kv_heads blocks;
+ * KV4 with protection adds one side block per kv head and layer. */
+int orc_cache_capacity(int fmt, const orc_layout* L, int32_t num_layers,
+                       const int32_t* seq_lens, int32_t n, uint64_t budget,
+                       uint64_t* total, int32_t* fit) {
+  if (!layout_ok(L) || num_layers < 1 || n < 0) return -1;
+  uint64_t page = (uint64_t)orc_block_bytes(fmt, L) * (uint64_t)L->num_kv_heads;
+  uint64_t side = 0;
+  if (fmt == ORC_FMT_KV4 && L->n_sink + L->n_recent > 0)
+    side = (uint64_t)orc_side_bytes(L) * (uint64_t)L->num_kv_heads;
+  uint64_t sum = 0;
+  int32_t k = 0;
+  int over = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    if (seq_lens[i] < 0) return -2;
+    uint64_t pages = ((uint64_t)seq_lens[i] + (uint64_t)L->page_size - 1) / (uint64_t)L->page_size;
+    sum += (pages * page + side) * (uint64_t)num_layers;
+    if (!over && sum <= budget) k = i + 1;
+    else over = 1;
+  }
+  *total = sum;
+  *fit = k;
+  return 0;
+}

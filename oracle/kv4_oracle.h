@@ -134,6 +134,12 @@ int orc_decode_mq(int fmt, const orc_layout* L, const uint8_t* pages,
                   const uint16_t* q, int32_t T, double sm_scale,
                   const int32_t* subset, int32_t n_subset, double* out,
                   double* lse, double* max_gap, int32_t nthreads);
+/* ---- capacity model -------------------------------------------------------- */
+/* Bytes of all n sequences (num_layers layers) and the largest k such that
+ * sequences 0 .. k-1 fit in budget bytes.  Returns 0, or < 0 on bad input. */
+int orc_cache_capacity(int fmt, const orc_layout* L, int32_t num_layers,
+                       const int32_t* seq_lens, int32_t n, uint64_t budget,
+                       uint64_t* total, int32_t* fit);
 #ifdef __cplusplus
 }
 #endif
