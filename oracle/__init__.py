@@ -84,7 +84,7 @@ def lib():
                                  ctypes.c_double, P, i32, P, P, P, i32, i32]
         L.orc_decode.restype = ctypes.c_int
         L.orc_decode_mq.argtypes = [ctypes.c_int, P, P, i64, P, i32, P, i32, P, P, i32, P, i32,
-                                    ctypes.c_double, P, i32, P, P, P, i32]
+                                    ctypes.c_double, P, i32, P, P, P, i32, i32]
         L.orc_decode_mq.restype = ctypes.c_int
         L.orc_cache_capacity.argtypes = [ctypes.c_int, P, i32, P, i32, ctypes.c_uint64, P, P]
         L.orc_cache_capacity.restype = ctypes.c_int
@@ -234,10 +234,11 @@ def decode(cache: HostCache, page_table, seq_lens, slot_ids, q_bf16, sm_scale=1.
 
 
 def decode_mq(cache: HostCache, page_table, seq_lens, slot_ids, q_bf16, num_queries: int,
-              sm_scale=1.0, subset=None, nthreads=0):
+              sm_scale=1.0, subset=None, nthreads=0, q_int8=False):
     """Multi-query decode: q_bf16 [B][T][Hq][D]; returns (out[n][T][Hq][D] fp64,
     lse[n][T][Hq] fp64, max merge gap).  Query t of sequence b sees the first
-    seq_lens[b] - T + t + 1 positions of the cache as it stands."""
+    seq_lens[b] - T + t + 1 positions of the cache as it stands.  q_int8: the
+    integer-query variant, as in decode."""
     lay = cache.lay
     T = int(num_queries)
     pt = np.ascontiguousarray(page_table, dtype=np.int32)
@@ -254,7 +255,7 @@ def decode_mq(cache: HostCache, page_table, seq_lens, slot_ids, q_bf16, num_quer
                              _ptr(cache.side), cache.num_slots, _ptr(pt), pt.shape[1], _ptr(sl),
                              _ptr(si), sl.size, _ptr(q), T, float(sm_scale), _ptr(sub),
                              0 if sub is None else sub.size, _ptr(out), _ptr(lse), _ptr(gap),
-                             int(nthreads))
+                             int(nthreads), 1 if q_int8 else 0)
     if rc != 0:
         raise ValueError(f"oracle multi-query decode rejected its input (code {rc})")
     return out, lse, float(gap[0])

@@ -581,7 +581,7 @@ int orc_decode_mq(int fmt, const orc_layout* L, const uint8_t* pages,
                   const int32_t* seq_lens, const int32_t* slot_ids, int32_t batch,
                   const uint16_t* q, int32_t T, double sm, const int32_t* subset,
                   int32_t n_subset, double* out, double* lse, double* max_gap,
-                  int32_t nthreads) {
+                  int32_t nthreads, int32_t q_int8) {
   if (!layout_ok(L) || T < 1) return -1;
   int D = L->head_dim, H = L->num_kv_heads, Hq = L->num_q_heads, g = Hq / H;
   int nseq = subset ? n_subset : batch;
@@ -616,7 +616,15 @@ int orc_decode_mq(int fmt, const orc_layout* L, const uint8_t* pages,
           int hq = h * g + j;
           double qv[128];
           const uint16_t* qrow = q + (((size_t)b * T + t) * Hq + hq) * D;
-          for (int c = 0; c < D; ++c) qv[c] = (double)orc_bf16_to_f32(qrow[c]);
+          if (q_int8) {
+            /* the integer-query variant, as in orc_decode */
+            int8_t qc[128];
+            uint16_t qs;
+            orc_quant_sym(qrow, D, 127, qc, &qs);
+            for (int c = 0; c < D; ++c) qv[c] = (double)qc[c] * orc_f16_to_f64(qs);
+          } else {
+            for (int c = 0; c < D; ++c) qv[c] = (double)orc_bf16_to_f32(qrow[c]);
+          }
           double gap;
           size_t o = ((size_t)i * T + t) * Hq + hq;
           orc_attend(n, D, qv, K, V, reg, sm, out + o * D, lse + o, &gap);

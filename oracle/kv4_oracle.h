@@ -126,14 +126,14 @@ int orc_decode(int fmt, const orc_layout* L, const uint8_t* pages,
  * query t of sequence b sees the first N - T + t + 1 positions of the cache
  * as it stands (N = seq_lens[b]), each read from where the cache holds it.
  * out[i][T][Hq][D], lse[i][T][Hq]; queries that see no position give 0 and
- * -inf.  T = 1 is orc_decode with q_int8 = 0. */
+ * -inf.  q_int8 as in orc_decode.  T = 1 is orc_decode. */
 int orc_decode_mq(int fmt, const orc_layout* L, const uint8_t* pages,
                   int64_t num_pages, const uint8_t* side, int32_t num_slots,
                   const int32_t* page_table, int32_t max_pages,
                   const int32_t* seq_lens, const int32_t* slot_ids, int32_t batch,
                   const uint16_t* q, int32_t T, double sm_scale,
                   const int32_t* subset, int32_t n_subset, double* out,
-                  double* lse, double* max_gap, int32_t nthreads);
+                  double* lse, double* max_gap, int32_t nthreads, int32_t q_int8);
 /* ---- capacity model -------------------------------------------------------- */
 /* Bytes of all n sequences (num_layers layers) and the largest k such that
  * sequences 0 .. k-1 fit in budget bytes.  Returns 0, or < 0 on bad input. */

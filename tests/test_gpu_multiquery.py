@@ -39,7 +39,8 @@ def _check(kv4, wl, T, label):
     sample = np.arange(wl.lengths.size)
     ocache, pt, lens = pu.compare_bytes(wl, sample)
     qh, og, lg = _run_mq(kv4, wl, T)
-    out64, lse64, gap = oracle.decode_mq(ocache, pt, lens, None, qh, T)
+    q_int8 = bool(wl.layout.flags & 2)  # the integer-query layout flag
+    out64, lse64, gap = oracle.decode_mq(ocache, pt, lens, None, qh, T, q_int8=q_int8)
     m = pu.metrics_from(og, lg, out64, lse64, gap)
     print(f"\nmulti-query {label} T={T}: rel_l2={m['rel_l2']:.3e} max_abs={m['max_abs']:.3e} "
           f"lse={m['lse_abs']:.3e}", flush=True)
@@ -115,6 +116,18 @@ def test_multiquery_group_sizes(kv4, hq, hkv):
             _check(kv4, wl, T, f"hq={hq} hkv={hkv}")
     finally:
         del wc.CONFIGS[91]
+
+
+@pytest.mark.parametrize("T", [2, 5])
+def test_multiquery_integer_query(kv4, T):
+    """The integer-query layout with several queries (one query per unit on
+    the integer path), Qwen shapes and the tiny shapes."""
+    from harness import build_from_host
+
+    wl = build_from_host(1, 0, lengths=np.array([700, 145, 1000, 60], dtype=np.int32), int8_query=True)
+    _check(kv4, wl, T, "qwen shapes int8 query")
+    wl = build_from_host(0, 0, lengths=np.array([300, 5, 21, 2], dtype=np.int32), int8_query=True)
+    _check(kv4, wl, T, "cfg0 int8 query")
 
 
 def test_multiquery_rejects_bad_counts(kv4):

@@ -76,6 +76,23 @@ def test_single_query_and_last_query_equal_decode(orc):
         np.testing.assert_array_equal(lse[:, T - 1], l1)
 
 
+def test_integer_query_last_query_equals_decode(orc):
+    """With the integer-query variant the last query still equals the
+    single-token decode with the same variant, and the variant differs from
+    the bf16 query."""
+    cfg = get_config(0)
+    lengths = np.array([300, 57, 17], dtype=np.int32)
+    cache, alloc, _ = build_host_cache(orc, cfg, orc.FMT_KV4, lengths)
+    T = 3
+    q = host_queries(cfg, 0, lengths.size, T)
+    out, lse, _ = orc.decode_mq(cache, alloc.page_table, lengths, None, q, T, q_int8=True)
+    o1, l1, _ = orc.decode(cache, alloc.page_table, lengths, None, _q_single(q, T - 1), q_int8=True)
+    np.testing.assert_array_equal(out[:, T - 1], o1)
+    np.testing.assert_array_equal(lse[:, T - 1], l1)
+    outf, _, _ = orc.decode_mq(cache, alloc.page_table, lengths, None, q, T)
+    assert not np.array_equal(out, outf)
+
+
 @pytest.mark.parametrize("fmt", [0, 1, 2], ids=["kv4-plain", "kv8", "bf16"])
 def test_unprotected_query_equals_decode_of_prefix(orc, fmt):
     """Without a side cache no row depends on the cache state, so query t
