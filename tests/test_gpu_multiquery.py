@@ -130,6 +130,19 @@ def test_multiquery_integer_query(kv4, T):
     _check(kv4, wl, T, "cfg0 int8 query")
 
 
+@pytest.mark.parametrize("S,R", [(16, 128), (0, 16), (5, 7), (0, 0)])
+def test_multiquery_slots_padding_and_protection(kv4, S, R):
+    """Qwen shapes (the multi-column kernel) with permuted side-cache slots,
+    spare pages in the pool, page tables wider than needed, and protection
+    widths that end inside a page."""
+    from harness import build_from_host
+
+    lengths = np.array([0, 1, 15, 16, 17, 143, 144, 145, 700, 1300], dtype=np.int32)
+    wl = build_from_host(1, 0, lengths=lengths, n_sink=S, n_recent=R, slot_perm_seed=5, extra_pages=7,
+                         max_pages=100)
+    _check(kv4, wl, 6, f"qwen shapes S={S} R={R} permuted slots")
+
+
 def test_multiquery_rejects_bad_counts(kv4):
     import torch
 
