@@ -59,6 +59,7 @@ static_assert(kChunkPages >= 1 && kChunkPages <= 64, "one lane holds one page id
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescale = 8.0f;  // re-reference the running max when it grows by 2^8
+constexpr int kAttnThreads = 512;  // single-query attention workgroup: two waves per SIMD of one CU
 
 enum Kind : int { kInt4Page = 0, kInt8Tile = 1, kBf16Page = 2 };
 
@@ -427,6 +428,10 @@ __device__ inline void step(Unit<D>& u, const Tile<KIND, D>& T0, const Tile<KIND
   // The running max of a head is only re-referenced when a score exceeds it
   // by 2^kRescale (then to the head's exact maximum so far), so p <= 2^8 and
   // the accumulators are rescaled rarely; the result does not depend on it.
+  // The accumulators are multiplied on every step (by 1 when the reference
+  // stays): a multiply only inside the branch makes the compiler copy every
+  // accumulator on the path that skips it.
+  float r01 = 1.0f, r23 = 1.0f;  // factor for accumulator elements 0-1 / 2-3
   if (__any(mx * sc > u.m + kRescale)) {
     mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
     mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
@@ -434,14 +439,16 @@ __device__ inline void step(Unit<D>& u, const Tile<KIND, D>& T0, const Tile<KIND
     const float alpha = (mn == u.m) ? 1.0f : __builtin_amdgcn_exp2f(u.m - mn);
     u.l *= alpha;
     u.m = mn;
+    r01 = head_value_for_acc<D>(alpha, lane, 0);
+    r23 = NG == 2 ? head_value_for_acc<D>(alpha, lane, 2) : r01;
+  }
 #pragma unroll
-    for (int e = 0; e < 4; ++e) u.corr[e] *= head_value_for_acc<D>(alpha, lane, e);
+  for (int e = 0; e < 4; ++e) u.corr[e] *= e < 2 ? r01 : r23;
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const int e0 = t / 2;
-      u.o[t][e0] *= head_value_for_acc<D>(alpha, lane, e0);
-      if constexpr (NG == 2) u.o[t][e0 + 2] *= head_value_for_acc<D>(alpha, lane, e0 + 2);
-    }
+  for (int t = 0; t < NT; ++t) {
+    const int e0 = t / 2;
+    u.o[t][e0] *= e0 < 2 ? r01 : r23;
+    if constexpr (NG == 2) u.o[t][e0 + 2] *= r23;
   }
 
   // p = 2^(sc*x - m); masked rows have x = -inf -> p = 0
@@ -631,6 +638,14 @@ __device__ inline int item_pages(const SeqWork& w, int chunk, int k) {
   return r > chunk ? chunk : (r < 0 ? 0 : r);
 }
 
+// Order key of an item that is not a full chunk: its pages plus the cost of
+// the side tiles its unit reads (the first item of a sequence), so that the
+// list ends on the cheapest units.
+__device__ inline int item_key(const SeqWork& w, int chunk, int k) {
+  const int c = item_pages(w, chunk, k) + (k == 0 ? kProtectedCost * w.prot_tiles : 0);
+  return c < kMaxChunkPages ? c : kMaxChunkPages;
+}
+
 // Work-item descriptor, two int4:
 //   [0] = {u, L, first middle page of the item, (chunk index << 8) | pages}
 //   [1] = {items of u, first partial slot of u, side slot, N}
@@ -676,8 +691,8 @@ __device__ inline unsigned long long block_exclusive_scan(unsigned long long v, 
 
 // One workgroup: chooses the chunk size from the total work, numbers the
 // partial slots of split sequences and writes the item descriptors: all full
-// chunks first, then the remaining (shorter) items in decreasing size, so the
-// round-robin assignment of units to waves ends on small items.  Each
+// chunks first, then the remaining (shorter) items in decreasing cost (pages
+// plus side tiles), so the units handed out last are the cheapest.  Each
 // thread handles sequences tid, tid + 1024, ...; the first one's lengths
 // are read once and kept.
 __global__ __launch_bounds__(1024) void worklist_kernel(DecodeParams p, int units_per_item) {
@@ -714,7 +729,7 @@ __global__ __launch_bounds__(1024) void worklist_kernel(DecodeParams p, int unit
       for (int k = 0; k < n; ++k) {
         const int pg = item_pages(w, chunk, k);
         if (pg == chunk) ++full;
-        else atomicAdd(&bucket[kMaxChunkPages - pg], 1u);
+        else atomicAdd(&bucket[kMaxChunkPages - item_key(w, chunk, k)], 1u);
       }
       split = n > 1 ? n * block_queries(p, b) : 0;
     }
@@ -728,7 +743,7 @@ __global__ __launch_bounds__(1024) void worklist_kernel(DecodeParams p, int unit
     run_full += int(tile & 0xFFFFFFFFull);
     run_split += int(tile >> 32);
   }
-  // positions of the shorter items, longest first (bucket i holds size
+  // positions of the shorter items, costliest first (bucket i holds key
   // kMaxChunkPages - i): an exclusive scan of the bucket counts by wave 0
   if (wid == 0) {
     const int i0 = 2 * lane, i1 = 2 * lane + 1;
@@ -752,7 +767,7 @@ __global__ __launch_bounds__(1024) void worklist_kernel(DecodeParams p, int unit
     uint32_t fpos = uint32_t(p.ws.merge_list[b]);
     for (int k = 0; k < n; ++k) {
       const int pg = item_pages(w, chunk, k);
-      const uint32_t pos = pg == chunk ? fpos++ : atomicAdd(&bucket[kMaxChunkPages - pg], 1u);
+      const uint32_t pos = pg == chunk ? fpos++ : atomicAdd(&bucket[kMaxChunkPages - item_key(w, chunk, k)], 1u);
       write_item(p, pos, b, w, chunk, k, n, pbase);
     }
     p.ws.item_count[b] = n;
@@ -803,7 +818,7 @@ __device__ inline ItemDesc decode_item(const RawItem& r) {
 }
 
 template <int FMT, int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KV4_WAVES_PER_EU, 8))) void attention_kernel(
+__global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(KV4_WAVES_PER_EU, 8))) void attention_kernel(
     DecodeParams p) {
   constexpr int NG = D / 32, HB = 16 / NG, NT = D / 16;
   constexpr bool KV4 = FMT == kFmtKV4 || FMT == kFmtKV4Q8;
@@ -817,16 +832,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KV4_WAVES_P
   const int S = KV4 ? p.n_sink : 0;
   const int R = KV4 ? p.n_recent : 0;
   // unit indices fit 32 bits: the host bounds the work list (items x units per item < 2^31)
-  const uint32_t units = p.ws.header[1] * uint32_t(UPI);
+  const uint32_t nitems = p.ws.header[1];
+  const uint32_t units = nitems * uint32_t(UPI);
   if (units == 0) return;
 
-  // Static round robin over the list (longest items first): in round k the
-  // waves hold units kN .. kN+N-1, so the kv heads of one item -- adjacent
-  // blocks of the same pages -- are read at the same time, which keeps DRAM
-  // rows open, and neighbouring waves have units of about the same size.  The
-  // next units are known in advance: the descriptor of unit k+2 and the page
-  // ids of unit k+1 are loaded when unit k starts.
-  const uint32_t nw = gridDim.x * (blockDim.x / kWave);
+  // One workgroup per CU, holding both waves of every SIMD.  Workgroup c owns
+  // one item of every C consecutive items of the list (costliest first), in
+  // serpentine order -- c, 2C - 1 - c, 2C + c, ... -- so the CUs get equal
+  // shares of every cost, and its waves take the units of those items (the kv
+  // heads of an item next to each other) from a counter in LDS.  The two waves
+  // of a SIMD do not progress at the same rate (the older one wins issue), so
+  // a fixed split between them would leave one wave per SIMD running alone at
+  // the end.  The next units are known in advance: the descriptor of unit k+2
+  // and the page ids of unit k+1 are loaded when unit k starts.
+  __shared__ uint32_t next_ticket;
+  if (threadIdx.x == 0) next_ticket = 0u;
+  __syncthreads();
+  auto grab = [&]() -> uint32_t {
+    uint32_t t = 0u;
+    if (lane == 0) t = atomicAdd(&next_ticket, 1u);
+    t = uint32_t(uniform(int(t)));
+    const uint32_t round = t / uint32_t(UPI), C = gridDim.x;
+    const uint32_t item = round * C + ((round & 1u) ? C - 1u - blockIdx.x : blockIdx.x);
+    return item < nitems ? item * uint32_t(UPI) + t % uint32_t(UPI) : units;
+  };
   auto item_of = [&](uint32_t t) -> uint32_t { return (t < units ? t : units - 1) / uint32_t(UPI); };
   // Page ids of an item, one per lane, and the pages it shares with the
   // sequence before or after it in the batch (the same physical page at the
@@ -852,14 +881,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KV4_WAVES_P
     }
     return Pids{v, __ballot(sh)};
   };
-  uint32_t t0 = blockIdx.x * (blockDim.x / kWave) + uniform(threadIdx.x / kWave);
+  uint32_t t0 = grab();
+  uint32_t t1 = grab();
   ItemDesc d0 = decode_item(load_item(p, item_of(t0)));
-  RawItem r1 = load_item(p, item_of(t0 + nw));
+  RawItem r1 = load_item(p, item_of(t1));
   Pids pid0 = fetch_pids(d0);
 
-  for (; t0 < units; t0 += nw) {
+  while (t0 < units) {
     // ---- run-ahead for the following units (fixed position, unconditional)
-    const RawItem r2 = load_item(p, item_of(t0 + 2 * nw));
+    const uint32_t t2 = grab();
+    const RawItem r2 = load_item(p, item_of(t2));
     const ItemDesc d1 = decode_item(r1);
     const Pids pid1 = fetch_pids(d1);
 
@@ -1049,6 +1080,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KV4_WAVES_P
       }
     }
     // ---- rotate the run-ahead state
+    t0 = t1;
+    t1 = t2;
     d0 = d1;
     r1 = r2;
     pid0 = pid1;
@@ -1573,8 +1606,8 @@ hipError_t launch_fd(DecodeParams p, unsigned phases, hipStream_t stream) {
   const bool mc = FMT == kFmtKV4 && D == 128 && p.nq > 1 && G <= 16 && 16 % G == 0;
   p.tq = mc ? 16 / G : 1;
   // the work list is sized for the attention grid, so both use the same count
-  const int blocks = cus * (mc ? blocks_per_cu(attention_mc_kernel) : blocks_per_cu(attention_kernel<FMT, D>));
-  p.resident_waves = blocks * 4;
+  const int blocks = mc ? cus * blocks_per_cu(attention_mc_kernel) : cus;
+  p.resident_waves = mc ? blocks * 4 : blocks * (kAttnThreads / kWave);
   if (phases & 1u) {
     const int units_per_item = mc ? p.num_kv_heads : p.num_kv_heads * ((G + HB - 1) / HB);
     hipLaunchKernelGGL(worklist_kernel, dim3(1), dim3(1024), 0, stream, p, units_per_item);
@@ -1585,7 +1618,7 @@ hipError_t launch_fd(DecodeParams p, unsigned phases, hipStream_t stream) {
     if (mc) {
       hipLaunchKernelGGL(attention_mc_kernel, dim3(blocks), dim3(256), 0, stream, p);
     } else {
-      hipLaunchKernelGGL((attention_kernel<FMT, D>), dim3(blocks), dim3(256), 0, stream, p);
+      hipLaunchKernelGGL((attention_kernel<FMT, D>), dim3(blocks), dim3(kAttnThreads), 0, stream, p);
     }
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;

@@ -30,10 +30,10 @@ struct AppendParams {
 hipError_t launch_append(int fmt, const AppendParams& p, int head_dim, hipStream_t stream);
 
 // Decode workspace: a header, per-sequence item table, the work items
-// (longest first), the list of sequences split over several items and the
+// (costliest first), the list of sequences split over several items and the
 // fp32 partial results of those items.
 struct DecodeWorkspace {
-  uint32_t* header;      // [0] unit counter, [1] items, [2] chunk pages, [3] split sequences
+  uint32_t* header;      // [0] unused, [1] items, [2] chunk pages, [3] split sequences
   int32_t* item_base;    // [batch] first partial slot of a split sequence
   int32_t* item_count;   // [batch]
   int32_t* merge_list;   // [batch] split sequences

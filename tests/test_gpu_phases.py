@@ -46,3 +46,33 @@ def test_plan_reused_across_layers(kv4, fmt):
     print(f"\nphased layer-1 parity fmt={fmt}: rel_l2={m['rel_l2']:.3e} max_abs={m['max_abs']:.3e} "
           f"lse={m['lse_abs']:.3e}", flush=True)
     pu.assert_within(m)
+
+
+@pytest.mark.parametrize("fmt", [0, 1], ids=["kv4", "kv8"])
+def test_attend_repeated_on_one_plan(kv4, fmt):
+    """The attention phase hands units out from counters in the workspace and
+    resets them when it ends: many ATTEND + MERGE pairs on one PLAN, with
+    different queries in between, each give the bits of a full decode."""
+    import torch
+
+    from harness import build_config
+
+    wl = build_config(1, fmt)
+    wl.step_append()
+    ws = torch.empty_like(wl.workspace)
+    ws.fill_(0x5A)
+    kv4.decode_phases(wl.cache, wl.batch, None, None, None, ws, kv4.PHASE_PLAN)
+    gen = torch.Generator(device="cpu").manual_seed(11)
+    for rep in range(6):
+        q = (torch.randn(wl.q.shape, generator=gen) * (1 + rep)).to(torch.bfloat16).to("cuda")
+        wl.q.copy_(q)
+        wl.decode()
+        torch.cuda.synchronize()
+        ref_out, ref_lse = wl.out.clone(), wl.lse.clone()
+        out = torch.full_like(wl.out, float("nan"))
+        lse = torch.full_like(wl.lse, float("nan"))
+        kv4.decode_phases(wl.cache, wl.batch, wl.q, out, lse, ws, kv4.PHASE_ATTEND)
+        kv4.decode_phases(wl.cache, wl.batch, wl.q, out, lse, ws, kv4.PHASE_MERGE)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref_out.view(torch.int16)), rep
+        assert torch.equal(lse.view(torch.int32), ref_lse.view(torch.int32)), rep
