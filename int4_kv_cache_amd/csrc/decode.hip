@@ -46,10 +46,13 @@ typedef uint32_t u32x4_t __attribute__((__vector_size__(16)));
 #define KV4_WAVES_PER_EU 2
 #endif
 #ifndef KV4_STAGES
-#define KV4_STAGES 3  // pipeline depth of the INT4 page loop
+#define KV4_STAGES 2  // pipeline depth of the INT4 page loop (side tiles: KV4_STAGES8)
 #endif
 #ifndef KV4_MC_STAGES
 #define KV4_MC_STAGES 1  // pipeline depth of the multi-column kernel (2 measured 1.3% slower)
+#endif
+#ifndef KV4_UNITS_PER_WAVE
+#define KV4_UNITS_PER_WAVE 8  // work-list granularity: chunk size from the total work
 #endif
 #ifndef KV4_STAGES8
 #define KV4_STAGES8 2  // pipeline depth of the INT8 tile loops
@@ -134,6 +137,35 @@ __device__ inline uint32_t nib_pair_at(uint32_t d, int k) {  // k in 0..3 (unrol
     default: return nib_pair<3>(d);
   }
 }
+
+#ifndef KV4_SHIFT64
+#define KV4_SHIFT64 1
+#endif
+#if KV4_SHIFT64
+static_assert(kEncShift == 0, "the paired conversion assumes the code nibble at the bottom of the bf16");
+// x >> S for a register pair in one instruction (the compiler splits a
+// 64-bit shift into two 32-bit ones).
+template <int S>
+__device__ inline uint64_t shr64(uint64_t x) {
+  uint64_t y;
+  asm("v_lshrrev_b64 %0, %1, %2" : "=v"(y) : "I"(S), "v"(x));
+  return y;
+}
+// Nibble pairs K of words a and b (b the next register), K = 1..3 from one
+// shift of the pair: the high word's nibbles that enter the top of the low
+// word land in bits the mask drops.
+template <int K>
+__device__ inline void nib_pairs2(uint32_t a, uint32_t b, uint32_t& oa, uint32_t& ob) {
+  if constexpr (K == 0) {
+    oa = nib_pair<0>(a);
+    ob = nib_pair<0>(b);
+  } else {
+    const uint64_t y = shr64<4 * K>((uint64_t(b) << 32) | a);
+    oa = (uint32_t(y) & kEncMask) ^ kEncBits;
+    ob = (uint32_t(y >> 32) & kEncMask) ^ kEncBits;
+  }
+}
+#endif
 
 // Cross-lane moves inside groups of 4 lanes (DPP quad permutations).
 __device__ inline float quad_xor1(float v) {
@@ -327,11 +359,24 @@ __device__ inline void qk_tile(const Unit<D>& u, const Tile<KIND, D>& T, float (
   } else if constexpr (KIND == kInt4Page) {
     const float c = -kEncConst * u.qsum;
     acc = f32x4_t{c, c, c, c};
+#if KV4_SHIFT64
+#pragma unroll
+    for (int t = 0; t < NG; t += 2) {
+      uint32_t a[4], b[4];
+      nib_pairs2<0>(T.k[t], T.k[t + 1], a[0], b[0]);
+      nib_pairs2<1>(T.k[t], T.k[t + 1], a[1], b[1]);
+      nib_pairs2<2>(T.k[t], T.k[t + 1], a[2], b[2]);
+      nib_pairs2<3>(T.k[t], T.k[t + 1], a[3], b[3]);
+      acc = mfma(bf8(a[0], a[1], a[2], a[3]), u.bq[t], acc);
+      acc = mfma(bf8(b[0], b[1], b[2], b[3]), u.bq[t + 1], acc);
+    }
+#else
 #pragma unroll
     for (int t = 0; t < NG; ++t) {
       const uint32_t d = T.k[t];
       acc = mfma(bf8(nib_pair<0>(d), nib_pair<1>(d), nib_pair<2>(d), nib_pair<3>(d)), u.bq[t], acc);
     }
+#endif
   } else if constexpr (KIND == kInt8Tile) {
     acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -500,6 +545,62 @@ __device__ inline void step(Unit<D>& u, const Tile<KIND, D>& T0, const Tile<KIND
     u.corr = mfma(a_hi, ones, u.corr);
     u.corr = mfma(a_lo, ones, u.corr);
   }
+#if KV4_SHIFT64
+  if constexpr (KIND == kInt4Page) {
+    // N-tiles j and j + 4 (head_dim 128) from one shift of each word pair:
+    // words (pair, w) and (pair, w + 1) are adjacent, holding tiles 4w + j.
+    // Head_dim 64: the two words of a tile are the two position pairs.
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint32_t a0, b0, a1, b1, a2, b2, a3, b3;
+      if (j == 0) {
+        nib_pairs2<0>(T0.v[0], T0.v[1], a0, b0);
+        nib_pairs2<0>(T1.v[0], T1.v[1], a1, b1);
+      } else if (j == 1) {
+        nib_pairs2<1>(T0.v[0], T0.v[1], a0, b0);
+        nib_pairs2<1>(T1.v[0], T1.v[1], a1, b1);
+      } else if (j == 2) {
+        nib_pairs2<2>(T0.v[0], T0.v[1], a0, b0);
+        nib_pairs2<2>(T1.v[0], T1.v[1], a1, b1);
+      } else {
+        nib_pairs2<3>(T0.v[0], T0.v[1], a0, b0);
+        nib_pairs2<3>(T1.v[0], T1.v[1], a1, b1);
+      }
+      if constexpr (D == 128) {
+        if (j == 0) {
+          nib_pairs2<0>(T0.v[2], T0.v[3], a2, b2);
+          nib_pairs2<0>(T1.v[2], T1.v[3], a3, b3);
+        } else if (j == 1) {
+          nib_pairs2<1>(T0.v[2], T0.v[3], a2, b2);
+          nib_pairs2<1>(T1.v[2], T1.v[3], a3, b3);
+        } else if (j == 2) {
+          nib_pairs2<2>(T0.v[2], T0.v[3], a2, b2);
+          nib_pairs2<2>(T1.v[2], T1.v[3], a3, b3);
+        } else {
+          nib_pairs2<3>(T0.v[2], T0.v[3], a2, b2);
+          nib_pairs2<3>(T1.v[2], T1.v[3], a3, b3);
+        }
+        // tile j: words (pair 0, w 0), (pair 1, w 0) of both tiles; tile j + 4: w 1
+        const bf16x8_t bv0 = bf8(a0, a2, a1, a3), bv1 = bf8(b0, b2, b1, b3);
+        f32x4_t c = u.o[j];
+        c = mfma(a_hi, bv0, c);
+        c = mfma(a_lo, bv0, c);
+        u.o[j] = c;
+        c = u.o[j + 4];
+        c = mfma(a_hi, bv1, c);
+        c = mfma(a_lo, bv1, c);
+        u.o[j + 4] = c;
+      } else {
+        const bf16x8_t bv = bf8(a0, b0, a1, b1);
+        f32x4_t c = u.o[j];
+        c = mfma(a_hi, bv, c);
+        c = mfma(a_lo, bv, c);
+        u.o[j] = c;
+      }
+    }
+    return;
+  }
+#endif
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     const bf16x8_t bv = v_operand<KIND, D>(T0, T1, t);
@@ -712,8 +813,8 @@ __global__ __launch_bounds__(1024) void worklist_kernel(DecodeParams p, int unit
   }
   unsigned long long total_pages = 0ull;
   (void)block_exclusive_scan(mine, part, total_pages);
-  // about 8 units per resident wave
-  const unsigned long long denom = 8ull * unsigned(p.resident_waves > 0 ? p.resident_waves : 1);
+  // about KV4_UNITS_PER_WAVE units per resident wave
+  const unsigned long long denom = unsigned(KV4_UNITS_PER_WAVE) * unsigned(p.resident_waves > 0 ? p.resident_waves : 1);
   unsigned long long cl = (total_pages * unsigned(units_per_item) + denom - 1) / denom;
   cl = cl < unsigned(kChunkPages) ? unsigned(kChunkPages) : (cl > unsigned(kMaxChunkPages) ? kMaxChunkPages : cl);
   const int chunk = int(cl);
