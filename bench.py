@@ -388,7 +388,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--variants", action="store_true",
                     help="also time kv8 / bf16 / plain INT4 / KV4 with the integer query")
     ap.add_argument("--no-cpu", action="store_true")
