@@ -918,6 +918,26 @@ __device__ inline ItemDesc decode_item(const RawItem& r) {
   return d;
 }
 
+// Per-CU unit pool.  One workgroup per CU holds both waves of every SIMD.
+// Workgroup c owns one item of every C consecutive items of the list
+// (costliest first), in serpentine order -- c, 2C - 1 - c, 2C + c, ... -- so
+// the CUs get equal shares of every cost, and its waves take the units of
+// those items (upi per item, next to each other) in ticket order from a
+// counter in LDS.  The two waves of a SIMD do not progress at the same rate
+// (the older one wins issue), so a fixed split between them would leave one
+// wave per SIMD running alone at the end.
+__device__ inline uint32_t pool_ticket(uint32_t* counter, int lane) {
+  uint32_t t = 0u;
+  if (lane == 0) t = atomicAdd(counter, 1u);
+  return uint32_t(uniform(int(t)));
+}
+// the unit of ticket t, or `units` past the end of the workgroup's share
+__device__ inline uint32_t pool_unit(uint32_t t, uint32_t upi, uint32_t nitems, uint32_t units) {
+  const uint32_t round = t / upi, C = gridDim.x;
+  const uint32_t item = round * C + ((round & 1u) ? C - 1u - blockIdx.x : blockIdx.x);
+  return item < nitems ? item * upi + t % upi : units;
+}
+
 template <int FMT, int D>
 __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(KV4_WAVES_PER_EU, 8))) void attention_kernel(
     DecodeParams p) {
@@ -937,26 +957,13 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(KV
   const uint32_t units = nitems * uint32_t(UPI);
   if (units == 0) return;
 
-  // One workgroup per CU, holding both waves of every SIMD.  Workgroup c owns
-  // one item of every C consecutive items of the list (costliest first), in
-  // serpentine order -- c, 2C - 1 - c, 2C + c, ... -- so the CUs get equal
-  // shares of every cost, and its waves take the units of those items (the kv
-  // heads of an item next to each other) from a counter in LDS.  The two waves
-  // of a SIMD do not progress at the same rate (the older one wins issue), so
-  // a fixed split between them would leave one wave per SIMD running alone at
-  // the end.  The next units are known in advance: the descriptor of unit k+2
-  // and the page ids of unit k+1 are loaded when unit k starts.
+  // Units come from the per-CU pool.  The next units are known in advance:
+  // the descriptor of unit k+2 and the page ids of unit k+1 are loaded when
+  // unit k starts.
   __shared__ uint32_t next_ticket;
   if (threadIdx.x == 0) next_ticket = 0u;
   __syncthreads();
-  auto grab = [&]() -> uint32_t {
-    uint32_t t = 0u;
-    if (lane == 0) t = atomicAdd(&next_ticket, 1u);
-    t = uint32_t(uniform(int(t)));
-    const uint32_t round = t / uint32_t(UPI), C = gridDim.x;
-    const uint32_t item = round * C + ((round & 1u) ? C - 1u - blockIdx.x : blockIdx.x);
-    return item < nitems ? item * uint32_t(UPI) + t % uint32_t(UPI) : units;
-  };
+  auto grab = [&]() -> uint32_t { return pool_unit(pool_ticket(&next_ticket, lane), UPI, nitems, units); };
   auto item_of = [&](uint32_t t) -> uint32_t { return (t < units ? t : units - 1) / uint32_t(UPI); };
   // Page ids of an item, one per lane, and the pages it shares with the
   // sequence before or after it in the batch (the same physical page at the
@@ -1467,7 +1474,7 @@ __device__ inline uint32_t rows4(int r, int lo, int hi) {
   return hi > lo ? ((1u << hi) - 1u) & ~((1u << lo) - 1u) : 0u;
 }
 
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KV4_WAVES_PER_EU, 8))) void attention_mc_kernel(
+__global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(KV4_WAVES_PER_EU, 8))) void attention_mc_kernel(
     DecodeParams p) {
   constexpr int D = 128, NT = 8;
   const int lane = threadIdx.x & (kWave - 1);
@@ -1475,10 +1482,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KV4_WAVES_P
   const int H = p.num_kv_heads, Hq = p.num_q_heads, G = Hq / H;
   const int S = p.n_sink, R = p.n_recent;
   const int T = p.nq, nqb = n_blocks(p);
-  const uint32_t units = p.ws.header[1] * uint32_t(H);
+  const uint32_t nitems = p.ws.header[1];
+  const uint32_t units = nitems * uint32_t(H);
   if (units == 0) return;
-  const uint32_t nw = gridDim.x * (blockDim.x / kWave);
-  for (uint32_t t0 = blockIdx.x * (blockDim.x / kWave) + uniform(threadIdx.x / kWave); t0 < units; t0 += nw) {
+  // units (item, kv head) from the per-CU pool
+  __shared__ uint32_t next_ticket;
+  if (threadIdx.x == 0) next_ticket = 0u;
+  __syncthreads();
+  auto grab = [&]() -> uint32_t { return pool_unit(pool_ticket(&next_ticket, lane), uint32_t(H), nitems, units); };
+  for (uint32_t t0 = grab(); t0 < units; t0 = grab()) {
     const ItemDesc d = decode_item(load_item(p, t0 / uint32_t(H)));
     const int h = int(t0 % uint32_t(H));
     const int bseq = d.b / nqb, tb = (d.b % nqb) * p.tq;  // sequence, first query of the block
@@ -1707,8 +1719,8 @@ hipError_t launch_fd(DecodeParams p, unsigned phases, hipStream_t stream) {
   const bool mc = FMT == kFmtKV4 && D == 128 && p.nq > 1 && G <= 16 && 16 % G == 0;
   p.tq = mc ? 16 / G : 1;
   // the work list is sized for the attention grid, so both use the same count
-  const int blocks = mc ? cus * blocks_per_cu(attention_mc_kernel) : cus;
-  p.resident_waves = mc ? blocks * 4 : blocks * (kAttnThreads / kWave);
+  const int blocks = cus;  // one workgroup per CU (the per-CU unit pool)
+  p.resident_waves = blocks * (kAttnThreads / kWave);
   if (phases & 1u) {
     const int units_per_item = mc ? p.num_kv_heads : p.num_kv_heads * ((G + HB - 1) / HB);
     hipLaunchKernelGGL(worklist_kernel, dim3(1), dim3(1024), 0, stream, p, units_per_item);
@@ -1717,7 +1729,7 @@ hipError_t launch_fd(DecodeParams p, unsigned phases, hipStream_t stream) {
   }
   if (phases & 2u) {
     if (mc) {
-      hipLaunchKernelGGL(attention_mc_kernel, dim3(blocks), dim3(256), 0, stream, p);
+      hipLaunchKernelGGL(attention_mc_kernel, dim3(blocks), dim3(kAttnThreads), 0, stream, p);
     } else {
       hipLaunchKernelGGL((attention_kernel<FMT, D>), dim3(blocks), dim3(kAttnThreads), 0, stream, p);
     }
