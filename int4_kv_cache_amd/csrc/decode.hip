@@ -63,6 +63,9 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescale = 8.0f;  // re-reference the running max when it grows by 2^8
 constexpr int kAttnThreads = 512;  // single-query attention workgroup: two waves per SIMD of one CU
+// fp32 partial of one (item, query head): o[D], m, l, two words of padding so
+// that rows start on 16-byte boundaries
+__host__ __device__ constexpr int part_stride(int D) { return D + 4; }
 
 enum Kind : int { kInt4Page = 0, kInt8Tile = 1, kBf16Page = 2 };
 
@@ -1169,7 +1172,7 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(KV
             const float v = lh > 0.f ? kEnc * o / lh : 0.f;
             p.out[(int64_t(b) * Hq + hq) * D + c] = f32_to_bf16_bits(v);
           } else {
-            p.ws.partials[(pslot * Hq + hq) * (D + 2) + c] = kEnc * o;
+            p.ws.partials[(pslot * Hq + hq) * part_stride(D) + c] = kEnc * o;
           }
         }
       }
@@ -1181,7 +1184,7 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(KV
         if (d.nitems == 1) {
           if (p.lse) p.lse[int64_t(b) * Hq + hq] = lt > 0.f ? (u.m + log2f(lt)) * kLn2 : -INFINITY;
         } else {
-          float* part = p.ws.partials + (pslot * Hq + hq) * (D + 2);
+          float* part = p.ws.partials + (pslot * Hq + hq) * part_stride(D);
           part[D] = u.m;
           part[D + 1] = lt;
         }
@@ -1606,7 +1609,7 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(KV
           if (d.nitems == 1) {
             p.out[row * D + c] = f32_to_bf16_bits(lh > 0.f ? kEnc * o / lh : 0.f);
           } else {
-            p.ws.partials[(slot * Hq + h * G + chj) * (D + 2) + c] = kEnc * o;
+            p.ws.partials[(slot * Hq + h * G + chj) * part_stride(D) + c] = kEnc * o;
           }
         }
       }
@@ -1616,7 +1619,7 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(KV
       if (d.nitems == 1) {
         if (p.lse) p.lse[row] = lt > 0.f ? (u.m + log2f(lt)) * kLn2 : -INFINITY;
       } else {
-        float* part = p.ws.partials + ((pbase + int64_t(qj) * d.nitems + d.ck) * Hq + h * G + hj) * (D + 2);
+        float* part = p.ws.partials + ((pbase + int64_t(qj) * d.nitems + d.ck) * Hq + h * G + hj) * part_stride(D);
         part[D] = u.m;
         part[D + 1] = lt;
       }
@@ -1632,61 +1635,75 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(KV
 // sequence of up to eight items costs one memory round trip.
 template <int D>
 __global__ __launch_bounds__(256) void merge_kernel(DecodeParams p) {
-  constexpr int E = D / kWave;  // output channels per lane
-  constexpr int K = 8;          // items per round
-  const int lane = threadIdx.x & (kWave - 1);
+  // A task is one (split block, query of the block, query head), merged by 16
+  // lanes: each lane holds E consecutive channels and reads every item's m
+  // and l itself, so the lanes of a task need no exchange and the four tasks
+  // of a wave proceed independently.
+  constexpr int QL = 16;      // lanes per task
+  constexpr int E = D / QL;   // channels per lane
+  constexpr int K = 8;        // items per round
+  constexpr int RS = part_stride(D);
+  const int sub = threadIdx.x & (QL - 1);
   const int Hq = p.num_q_heads;
-  const int64_t nw = int64_t(gridDim.x) * (blockDim.x / kWave);
+  const int64_t nt = int64_t(gridDim.x) * (blockDim.x / QL);
   const int nqb = n_blocks(p);
   const int64_t per = int64_t(p.tq) * Hq;  // (query of the block, head) pairs
   const int64_t tasks = int64_t(p.ws.header[3]) * per;
-  for (int64_t w = int64_t(blockIdx.x) * (blockDim.x / kWave) + threadIdx.x / kWave; w < tasks; w += nw) {
+  for (int64_t w = int64_t(blockIdx.x) * (blockDim.x / QL) + threadIdx.x / QL; w < tasks; w += nt) {
     const int u = p.ws.merge_list[w / per];
     const int j = int((w % per) / Hq), hq = int(w % Hq);
     if (j >= block_queries(p, u)) continue;
     const int b = (u / nqb) * p.nq + (u % nqb) * p.tq + j;  // output row: query t of sequence b
     const int n = p.ws.item_count[u];
-    const float* base = p.ws.partials + ((int64_t(p.ws.item_base[u]) + int64_t(j) * n) * Hq + hq) * (D + 2);
-    const int64_t stride = int64_t(Hq) * (D + 2);
+    const float* base = p.ws.partials + ((int64_t(p.ws.item_base[u]) + int64_t(j) * n) * Hq + hq) * RS;
+    const int64_t stride = int64_t(Hq) * RS;
     float M = -INFINITY, l = 0.f, o[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) o[e] = 0.f;
     for (int i0 = 0; i0 < n; i0 += K) {
       const int cnt = n - i0 < K ? n - i0 : K;
-      float mi = -INFINITY, li = 0.f;
-      if (lane < cnt) {
-        const float* pm = base + (i0 + lane) * stride;
-        mi = pm[D];
-        li = pm[D + 1];
-      }
-      float v[K][E];
+      float mi[K], li[K], v[K][E];
 #pragma unroll
       for (int k = 0; k < K; ++k) {
-        const float* pk = base + (i0 + (k < cnt ? k : 0)) * stride + lane * E;
+        const float* row = base + (i0 + (k < cnt ? k : 0)) * stride;
+        const float2 ml = *reinterpret_cast<const float2*>(row + D);
+        // an item without context rows, or none, weighs 0
+        mi[k] = (k < cnt && ml.y > 0.f) ? ml.x : -INFINITY;
+        li[k] = ml.y;
 #pragma unroll
-        for (int e = 0; e < E; ++e) v[k][e] = pk[e];
+        for (int q = 0; q < E / 4; ++q) {
+          const float4 x = *reinterpret_cast<const float4*>(row + sub * E + 4 * q);
+          v[k][4 * q] = x.x;
+          v[k][4 * q + 1] = x.y;
+          v[k][4 * q + 2] = x.z;
+          v[k][4 * q + 3] = x.w;
+        }
       }
-      if (!(li > 0.f)) mi = -INFINITY;  // an item without context rows
-      const float mc = wave_max<kWave>(mi);
+      float mc = mi[0];
+#pragma unroll
+      for (int k = 1; k < K; ++k) mc = fmaxf(mc, mi[k]);
       const float Mn = fmaxf(M, mc);
       if (Mn == -INFINITY) continue;
       const float sc = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
-      const float wi = mi == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mi - Mn);
-      l = l * sc + wave_sum<kWave>(wi * li);
+      l *= sc;
 #pragma unroll
       for (int e = 0; e < E; ++e) o[e] *= sc;
 #pragma unroll
       for (int k = 0; k < K; ++k) {
-        const float a = __shfl(wi, k, kWave);  // 0 for k >= cnt
+        const float a = mi[k] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mi[k] - Mn);
+        l = fmaf(a, li[k], l);
 #pragma unroll
         for (int e = 0; e < E; ++e) o[e] = fmaf(a, v[k][e], o[e]);
       }
       M = Mn;
     }
     const float inv = l > 0.f ? 1.0f / l : 0.f;
+    uint16_t* orow = p.out + (int64_t(b) * Hq + hq) * D + sub * E;
 #pragma unroll
-    for (int e = 0; e < E; ++e) p.out[(int64_t(b) * Hq + hq) * D + lane * E + e] = f32_to_bf16_bits(o[e] * inv);
-    if (p.lse && lane == 0) p.lse[int64_t(b) * Hq + hq] = l > 0.f ? (M + log2f(l)) * kLn2 : -INFINITY;
+    for (int e = 0; e < E; e += 2)
+      *reinterpret_cast<uint32_t*>(orow + e) =
+          uint32_t(f32_to_bf16_bits(o[e] * inv)) | (uint32_t(f32_to_bf16_bits(o[e + 1] * inv)) << 16);
+    if (p.lse && sub == 0) p.lse[int64_t(b) * Hq + hq] = l > 0.f ? (M + log2f(l)) * kLn2 : -INFINITY;
   }
 }
 
@@ -1772,7 +1789,7 @@ size_t decode_workspace_bytes(int32_t batch, int32_t max_pages, int32_t num_q_he
   size_t s = 256;                                   // header
   s += 3 * align256(sizeof(int32_t) * size_t(batch));  // item_base, item_count, merge_list
   s += align256(2 * sizeof(int4) * size_t(max_items)); // items
-  s += align256(sizeof(float) * size_t(max_items) * num_q_heads * (head_dim + 2));
+  s += align256(sizeof(float) * size_t(max_items) * num_q_heads * part_stride(head_dim));
   return s;
 }
 

@@ -38,7 +38,7 @@ struct DecodeWorkspace {
   int32_t* item_count;   // [batch]
   int32_t* merge_list;   // [batch] split sequences
   int4* items;           // [max_items][2] work-item descriptors (two int4 each)
-  float* partials;       // [max_items][num_q_heads][head_dim + 2]
+  float* partials;       // [max_items][num_q_heads][head_dim + 4]: o, m, l, padding
   int64_t max_items;
 };
 
