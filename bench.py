@@ -402,7 +402,7 @@ def main():
                     help="only run a plain 1 GiB device copy 3 times (scales the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "this library is measured on one GPU; --gpus must be 1 (the path would shard over sequences or kv heads without exchange inside attention)"}))
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()

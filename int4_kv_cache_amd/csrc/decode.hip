@@ -968,29 +968,36 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(KV
   __syncthreads();
   auto grab = [&]() -> uint32_t { return pool_unit(pool_ticket(&next_ticket, lane), UPI, nitems, units); };
   auto item_of = [&](uint32_t t) -> uint32_t { return (t < units ? t : units - 1) / uint32_t(UPI); };
-  // Page ids of an item, one per lane, and the pages it shares with the
-  // sequence before or after it in the batch (the same physical page at the
-  // same index: a shared prompt), as a lane mask.
+  // Page ids of an item, one per lane, loaded one unit ahead as raw page-table
+  // words: this lane's page and the pages at the same index of the work
+  // indices before and after it (other queries of the sequence, or the
+  // neighbouring sequences).  The loads are unconditional (clamped indices)
+  // and every check is made when the unit starts, so nothing waits for them
+  // early.  A page is shared when a neighbour holds the same physical page at
+  // the same index: a shared prompt.
   struct Pids {
-    int pid;
-    uint64_t shared;
+    int x, xp, xn;
   };
   auto fetch_pids = [&](const ItemDesc& d) -> Pids {
-    int v = 0;
-    bool sh = false;
-    if (lane < d.npg) {
-      const int col = d.first + lane;
-      const int64_t x = p.page_table[int64_t(d.b / p.nq) * p.max_pages + col];  // tq = 1: u = b * nq + t
-      v = (x < 0 || x >= p.num_pages) ? -1 : int(x);
-      if constexpr (KV4 && KV4_NT_LOADS) {
-        // the neighbouring work indices: other queries of this sequence or
-        // the sequences before and after it
-        const int xp = d.b > 0 ? p.page_table[int64_t((d.b - 1) / p.nq) * p.max_pages + col] : -1;
-        const int xn = d.b + 1 < p.batch * p.nq ? p.page_table[int64_t((d.b + 1) / p.nq) * p.max_pages + col] : -1;
-        sh = v >= 0 && (xp == v || xn == v);
-      }
+    const int col = d.first + lane < p.max_pages ? d.first + lane : p.max_pages - 1;
+    const int nv = p.batch * p.nq;
+    const int bp = d.b > 0 ? d.b - 1 : 0, bn = d.b + 1 < nv ? d.b + 1 : d.b;
+    Pids r;
+    r.x = p.page_table[int64_t(d.b / p.nq) * p.max_pages + col];  // tq = 1: u = b * nq + t
+    r.xp = r.xn = -1;
+    if constexpr (KV4 && KV4_NT_LOADS) {
+      r.xp = p.page_table[int64_t(bp / p.nq) * p.max_pages + col];
+      r.xn = p.page_table[int64_t(bn / p.nq) * p.max_pages + col];
     }
-    return Pids{v, __ballot(sh)};
+    return r;
+  };
+  // this lane's page id (-1 past the item or out of range) and the lane mask
+  // of shared pages
+  auto resolve_pids = [&](const Pids& r, const ItemDesc& d, int& pid, uint64_t& shared) {
+    const bool ok = lane < d.npg && r.x >= 0 && int64_t(r.x) < p.num_pages;
+    pid = ok ? r.x : -1;
+    const bool sh = ok && ((d.b > 0 && r.xp == r.x) || (d.b + 1 < p.batch * p.nq && r.xn == r.x));
+    shared = __ballot(KV4 && KV4_NT_LOADS && sh);
   };
   uint32_t t0 = grab();
   uint32_t t1 = grab();
@@ -999,6 +1006,10 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(KV
   Pids pid0 = fetch_pids(d0);
 
   while (t0 < units) {
+    // this unit's page ids (loaded during the previous unit)
+    int pid0v;
+    uint64_t shared0;
+    resolve_pids(pid0, d0, pid0v, shared0);
     // ---- run-ahead for the following units (fixed position, unconditional)
     const uint32_t t2 = grab();
     const RawItem r2 = load_item(p, item_of(t2));
@@ -1132,13 +1143,13 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(KV
     if (d.npg > 0) {
       constexpr int ST = MAIN == kInt4Page ? KV4_STAGES : (MAIN == kInt8Tile ? KV4_STAGES8 : 1);
       // pages [0, ns) of the item are shared with a neighbouring sequence
-      const int ns = ~pid0.shared == 0ull ? kWave : int(__builtin_ctzll(~pid0.shared));
+      const int ns = ~shared0 == 0ull ? kWave : int(__builtin_ctzll(~shared0));
       auto ptr = [&](int i) {
-        const int pid = __builtin_amdgcn_readlane(pid0.pid, i);
+        const int pid = __builtin_amdgcn_readlane(pid0v, i);
         return p.pages + (int64_t(pid < 0 ? 0 : pid) * H + h) * p.block_bytes;
       };
       auto mask = [&](int i) {
-        const int pid = __builtin_amdgcn_readlane(pid0.pid, i);
+        const int pid = __builtin_amdgcn_readlane(pid0v, i);
         const int p0 = (d.first + i) * kPage;
         return pid < 0 ? 0u : range_mask(g.mb - p0, g.me - p0);
       };
