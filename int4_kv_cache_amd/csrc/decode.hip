@@ -1148,10 +1148,15 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(KV
         const int pid = __builtin_amdgcn_readlane(pid0v, i);
         return p.pages + (int64_t(pid < 0 ? 0 : pid) * H + h) * p.block_bytes;
       };
+      // Row masks: the region [mb, me) can cut only the item's first and last
+      // pages; a page whose id is out of range contributes nothing.
+      const uint64_t okm = __ballot(pid0v >= 0);
+      const int pf = d.first * kPage, il = d.npg - 1;
+      const uint32_t m_first = range_mask(g.mb - pf, g.me - pf);
+      const uint32_t m_last = range_mask(g.mb - pf - il * kPage, g.me - pf - il * kPage);
       auto mask = [&](int i) {
-        const int pid = __builtin_amdgcn_readlane(pid0v, i);
-        const int p0 = (d.first + i) * kPage;
-        return pid < 0 ? 0u : range_mask(g.mb - p0, g.me - p0);
+        const uint32_t m = i == 0 ? m_first : (i == il ? m_last : 0xFFFFu);
+        return ((okm >> i) & 1ull) ? m : 0u;
       };
       if constexpr (MAIN == kInt4Page && KV4_NT_LOADS) {
         run_tiles<MAIN, D, ST, Q8, false>(u, ns, ptr, mask, lane, setup);
