@@ -177,6 +177,21 @@ __device__ inline float quad_xor1(float v) {
 __device__ inline float quad_xor2(float v) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true));
 }
+// value of lane E of this lane's group of 4
+template <int E>
+__device__ inline float quad_bcast(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), E * 0x55, 0xF, 0xF, true));
+}
+// Reduce-scatter over groups of 4 lanes: lane g of a group gets the sum over
+// the group of element x[g].  Two exchange levels (partner g ^ 2, then g ^ 1);
+// at each, a lane keeps the half of its elements that its own index selects
+// and adds the partner's copy of the same half.
+__device__ inline float quad_reduce_scatter(const float (&x)[4], int lane) {
+  const bool b2 = (lane & 2) != 0, b1 = (lane & 1) != 0;
+  const float y0 = (b2 ? x[2] : x[0]) + quad_xor2(b2 ? x[0] : x[2]);
+  const float y1 = (b2 ? x[3] : x[1]) + quad_xor2(b2 ? x[1] : x[3]);
+  return (b1 ? y1 : y0) + quad_xor1(b1 ? y0 : y1);
+}
 
 // ------------------------------------------------------------ tile loads --
 // Every load is (uniform block base) + (per-lane 32-bit offset, fixed for the
@@ -440,6 +455,9 @@ __device__ inline float head_value_for_acc(float v, int lane, int e) {
   }
 }
 
+template <int KIND, int D>
+__device__ inline void pv_step(Unit<D>& u, const Tile<KIND, D>& T0, const Tile<KIND, D>& T1, const float (&pr)[8]);
+
 // One step: two 16-row tiles (32 positions).  mask0/mask1: 16-bit row masks.
 template <int KIND, int D, bool MASKED, bool Q8>
 __device__ inline void step(Unit<D>& u, const Tile<KIND, D>& T0, const Tile<KIND, D>& T1, uint32_t mask0,
@@ -452,7 +470,53 @@ __device__ inline void step(Unit<D>& u, const Tile<KIND, D>& T0, const Tile<KIND
   float x0[4], x1[4];
   qk_tile<KIND, D, Q8>(u, T0, x0);
   qk_tile<KIND, D, Q8>(u, T1, x1);
-  // sum the per-group partial scores of a head (lanes 4h..4h+3 or 2h..2h+1)
+  // score (log2 units) = sc * x; INT4 partials carry the encoding's 1/kEnc
+  const float sc = (KIND == kInt4Page && !Q8) ? kEnc * u.qk_scale : u.qk_scale;
+  if constexpr (NG == 4) {
+    // Lanes 4h..4h+3 hold the four group partials of head h for positions
+    // 4kg..4kg+3.  Lane 4h+g sums position 4kg+g only and takes its
+    // exponential; the PV operand then gathers the four probabilities of the
+    // group of lanes.  One exponential per position instead of four.
+    float z0 = quad_reduce_scatter(x0, lane), z1 = quad_reduce_scatter(x1, lane);
+    if ((mask0 & mask1) != 0xFFFFu) {  // wave-uniform: only partial steps are masked
+      const int g = lane & 3;
+      z0 = ((va0 >> g) & 1u) ? z0 : -INFINITY;
+      z1 = ((va1 >> g) & 1u) ? z1 : -INFINITY;
+    }
+    float mx = fmaxf(z0, z1);
+    float r = 1.0f;
+    if (__any(mx * sc > u.m + kRescale)) {
+      mx = fmaxf(mx, quad_xor1(mx));
+      mx = fmaxf(mx, quad_xor2(mx));
+      mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+      const float mn = fmaxf(u.m, mx * sc);
+      const float alpha = (mn == u.m) ? 1.0f : __builtin_amdgcn_exp2f(u.m - mn);
+      u.l *= alpha;
+      u.m = mn;
+      r = head_value_for_acc<D>(alpha, lane, 0);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) u.corr[e] *= r;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) u.o[t][t / 2] *= r;
+    const float mneg = u.m == -INFINITY ? 0.0f : -u.m;
+    const float p0 = __builtin_amdgcn_exp2f(fmaf(z0, sc, mneg));
+    const float p1 = __builtin_amdgcn_exp2f(fmaf(z1, sc, mneg));
+    u.l += p0 + p1;
+    float pr[8];
+    pr[0] = quad_bcast<0>(p0);
+    pr[1] = quad_bcast<1>(p0);
+    pr[2] = quad_bcast<2>(p0);
+    pr[3] = quad_bcast<3>(p0);
+    pr[4] = quad_bcast<0>(p1);
+    pr[5] = quad_bcast<1>(p1);
+    pr[6] = quad_bcast<2>(p1);
+    pr[7] = quad_bcast<3>(p1);
+    pv_step<KIND, D>(u, T0, T1, pr);
+    return;
+  }
+  // head_dim 64: sum the two group partials of a head (lanes 2h, 2h+1)
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     x0[e] += quad_xor1(x0[e]);
@@ -470,8 +534,6 @@ __device__ inline void step(Unit<D>& u, const Tile<KIND, D>& T0, const Tile<KIND
     }
   }
   float mx = max3(max3(x0[0], x0[1], x0[2]), max3(x0[3], x1[0], x1[1]), max3(x1[2], x1[3], -INFINITY));
-  // score (log2 units) = sc * x; INT4 partials carry the encoding's 1/kEnc
-  const float sc = (KIND == kInt4Page && !Q8) ? kEnc * u.qk_scale : u.qk_scale;
 
   // The running max of a head is only re-referenced when a score exceeds it
   // by 2^kRescale (then to the head's exact maximum so far), so p <= 2^8 and
@@ -508,7 +570,14 @@ __device__ inline void step(Unit<D>& u, const Tile<KIND, D>& T0, const Tile<KIND
     pr[e + 4] = __builtin_amdgcn_exp2f(fmaf(x1[e], sc, mneg));
   }
   u.l += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
+  pv_step<KIND, D>(u, T0, T1, pr);
+}
 
+// PV of one step from the probabilities pr[e] of this lane's head at the
+// positions of its A operand (4kg + e of T0, then of T1).
+template <int KIND, int D>
+__device__ inline void pv_step(Unit<D>& u, const Tile<KIND, D>& T0, const Tile<KIND, D>& T1, const float (&pr)[8]) {
+  constexpr int NT = D / 16;
   // A operand of PV: p * v_scale of (position, this row's group), split into
   // bf16 hi + lo.  INT8 and bf16 rows carry the 1/kEnc of the INT4 encoding.
   float ap[8];
@@ -1169,6 +1238,10 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(KV
 
     // ---- finish: per-head denominators, then output or partial
     float lt = u.l;
+    if constexpr (NG == 4) {  // each lane of a head's group of 4 summed its own positions
+      lt += quad_xor1(lt);
+      lt += quad_xor2(lt);
+    }
     lt += __shfl_xor(lt, 16, kWave);
     lt += __shfl_xor(lt, 32, kWave);
     const int64_t pslot = int64_t(d.pbase) + d.ck;
