@@ -9,8 +9,9 @@ and already resident in HBM when timing starts.
 
 Prints one JSON line.  `value` is context tokens per second (sum of the
 sequences' context lengths / step time).  The decode runs as its three phases
-(kv4_decode_phases: plan, attend, merge), each bracketed by HIP events on the
-stream it runs on.  `roofline` is for the dominant kernel, the attention
+(kv4_decode_phases: plan, attend, merge); in the timed region the attention
+launch is bracketed by HIP events on the stream it runs on, and a second pass
+of the same steps times every phase.  `roofline` is for the dominant kernel, the attention
 kernel of the ATTEND phase, against the 8 TB/s HBM peak with its algorithmic
 bytes; `traffic` is the HBM bytes per launch from the committed rocprofv3
 counter runs (null once the kernel sources differ from the ones measured).
@@ -118,10 +119,17 @@ def measured_traffic():
 def time_steps(wl, steps, warmup, append=True):
     """Time `steps` decode steps after `warmup` untimed ones.
 
-    A step is kv4_append of one token per sequence (if `append`), then the
-    decode as its three phases (plan, attend, merge) on the same stream, each
-    bracketed by HIP events on that stream.  Returns the mean ms per step over
-    the whole timed region and per-step ms arrays of every phase.
+    A step is the append of one token per sequence (if `append`) and the
+    decode as its three phases (plan, attend, merge) on one stream: with an
+    append, kv4_append_decode_phases stores the tokens and makes the plan in
+    one launch, then kv4_decode_phases runs ATTEND and MERGE.  In the timed
+    region only the attention launch is bracketed by HIP events on that
+    stream: every event record costs the stream 2-3 us, so the phases are
+    timed in a second pass of the same steps with an event between every
+    phase (there the append and the plan run as separate launches, to show
+    each).  Returns the mean ms per step over the timed region, and per-step
+    ms arrays of every phase (attend from the timed region, the rest and
+    "step_with_phase_events" from the second pass).
     """
     import torch
 
@@ -132,16 +140,35 @@ def time_steps(wl, steps, warmup, append=True):
     def phase(mask):
         kv4.decode_phases(wl.cache, wl.batch, wl.q, wl.out, wl.lse, wl.workspace, mask)
 
+    def new_events(n, k):
+        return [[torch.cuda.Event(enable_timing=True) for _ in range(k)] for _ in range(n)]
+
     for _ in range(warmup):
         if append:
             wl.step_append()
         wl.decode()
     torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    ev = new_events(steps, 2)
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0.record(stream)
+    for e in ev:
+        if append:
+            kv4.append_decode_phases(wl.cache, wl.batch, wl.step_k, wl.step_v, wl.step_cu, wl.q, wl.out, wl.lse,
+                                     wl.workspace, kv4.PHASE_PLAN)
+        else:
+            phase(kv4.PHASE_PLAN)
+        e[0].record(stream)
+        phase(kv4.PHASE_ATTEND)
+        e[1].record(stream)
+        phase(kv4.PHASE_MERGE)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    attend = np.array([e[0].elapsed_time(e[1]) for e in ev])
+    # breakdown pass (not the timed region)
+    ev = new_events(steps, 5)
     for e in ev:
         e[0].record(stream)
         if append:
@@ -153,12 +180,12 @@ def time_steps(wl, steps, warmup, append=True):
         e[3].record(stream)
         phase(kv4.PHASE_MERGE)
         e[4].record(stream)
-    t1.record(stream)
     torch.cuda.synchronize()
-    total_ms = t0.elapsed_time(t1)
     ph = {name: np.array([e[i].elapsed_time(e[i + 1]) for e in ev])
-          for i, name in enumerate(("append", "plan", "attend", "merge"))}
+          for i, name in enumerate(("append", "plan", "attend_breakdown", "merge"))}
+    ph["attend"] = attend
     ph["decode"] = ph["plan"] + ph["attend"] + ph["merge"]
+    ph["step_with_phase_events"] = np.array([e[0].elapsed_time(e[4]) for e in ev])
     return total_ms / steps, ph
 
 
@@ -446,6 +473,7 @@ def main():
                    "global_batch": int(wl.lengths.size), "ctx_tokens": ctx,
                    "append_us": us["append"], "plan_us": us["plan"], "attend_us": us["attend"],
                    "merge_us": us["merge"], "decode_us": us["decode"],
+                   "step_us_with_phase_events": us["step_with_phase_events"],
                    "decode_us_median": float(np.median(ph["decode"])) * 1e3,
                    "decode_hbm_frac": abytes / (us["decode"] * 1e-6) / 1e9 / HBM_PEAK_GBS,
                    "decode_algorithmic_bytes": abytes},

@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define KV4_ABI_VERSION 3
+#define KV4_ABI_VERSION 4
 
 typedef enum {
   KV4_OK = 0,
@@ -253,6 +253,41 @@ kv4_status kvbf16_decode_phases(const kv4_layout* layout, const kv4_cache* cache
                                 float softmax_scale, uint16_t* out, float* lse,
                                 void* workspace, size_t workspace_bytes,
                                 uint32_t phases, hipStream_t stream);
+
+/* ---- append + decode in one call ------------------------------------------------
+ * One layer's decode step: kv4_append(k_new, v_new, cu_new, total_new) and
+ * then kv4_decode_phases(..., phases) on the same batch, with the same results
+ * bit for bit.  When `phases` holds KV4_PHASE_PLAN, the plan is made in the
+ * launch that stores the new tokens (one extra workgroup): the plan reads
+ * only seq_lens, the page table and slot_ids, which the append does not
+ * write, so the two latency-bound pieces overlap.  The pages describe the
+ * decode step as appending the new token to the paged cache and attending
+ * over it ([NEWS] Interpretation para 3); putting both in one call is this
+ * library's.  Arguments, errors and contracts are those of the two calls
+ * (the cache is required even for phases = KV4_PHASE_PLAN); every argument
+ * is checked before anything is launched.  total_new = 0 runs the decode
+ * phases alone. */
+kv4_status kv4_append_decode_phases(const kv4_layout* layout, const kv4_cache* cache,
+                                    const kv4_batch* batch, const uint16_t* k_new,
+                                    const uint16_t* v_new, const int32_t* cu_new,
+                                    int32_t total_new, const uint16_t* q,
+                                    float softmax_scale, uint16_t* out, float* lse,
+                                    void* workspace, size_t workspace_bytes,
+                                    uint32_t phases, hipStream_t stream);
+kv4_status kv8_append_decode_phases(const kv4_layout* layout, const kv4_cache* cache,
+                                    const kv4_batch* batch, const uint16_t* k_new,
+                                    const uint16_t* v_new, const int32_t* cu_new,
+                                    int32_t total_new, const uint16_t* q,
+                                    float softmax_scale, uint16_t* out, float* lse,
+                                    void* workspace, size_t workspace_bytes,
+                                    uint32_t phases, hipStream_t stream);
+kv4_status kvbf16_append_decode_phases(const kv4_layout* layout, const kv4_cache* cache,
+                                       const kv4_batch* batch, const uint16_t* k_new,
+                                       const uint16_t* v_new, const int32_t* cu_new,
+                                       int32_t total_new, const uint16_t* q,
+                                       float softmax_scale, uint16_t* out, float* lse,
+                                       void* workspace, size_t workspace_bytes,
+                                       uint32_t phases, hipStream_t stream);
 
 /* ---- multi-query decode ------------------------------------------------------
  * T = num_queries query tokens per sequence (1 <= T <= KV4_MAX_QUERIES): the

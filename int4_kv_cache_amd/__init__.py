@@ -60,6 +60,7 @@ EXPORTS = [
     "kv4_decode_attention", "kv8_decode_attention", "kvbf16_decode_attention",
     "kv4_decode_phases", "kv8_decode_phases", "kvbf16_decode_phases",
     "kv4_decode_attention_mq", "kv8_decode_attention_mq", "kvbf16_decode_attention_mq",
+    "kv4_append_decode_phases", "kv8_append_decode_phases", "kvbf16_append_decode_phases",
     "kv4_cache_capacity",
     "kv4_probe_blocks", "kv4_hbm_read_probe",
 ]
@@ -97,6 +98,9 @@ def load(path: Optional[str] = None):
         f = getattr(L, f"{pre}_decode_attention_mq")
         f.restype = ctypes.c_int
         f.argtypes = [P, P, P, P, i32, ctypes.c_float, P, P, P, sz, P]
+        f = getattr(L, f"{pre}_append_decode_phases")
+        f.restype = ctypes.c_int
+        f.argtypes = [P, P, P, P, P, P, i32, P, ctypes.c_float, P, P, P, sz, ctypes.c_uint32, P]
     L.kv4_decode_workspace_size.restype = ctypes.c_int
     L.kv4_decode_workspace_size.argtypes = [P, i32, i32, ctypes.POINTER(sz)]
     L.kv4_cache_capacity.restype = ctypes.c_int
@@ -257,6 +261,20 @@ def decode_phases(cache: Cache, batch: Batch, q, out, lse, workspace, phases: in
     st = getattr(load(), fn)(ctypes.byref(lay), ctypes.byref(cd), ctypes.byref(bd), _ptr(q),
                              float(softmax_scale), _ptr(out), _ptr(lse), _ptr(workspace),
                              int(workspace.numel()), int(phases), _stream(stream))
+    _check(fn, st)
+
+
+def append_decode_phases(cache: Cache, batch: Batch, k_new, v_new, cu_new, q, out, lse, workspace,
+                         phases: int = PHASE_PLAN | PHASE_ATTEND | PHASE_MERGE, softmax_scale: float = 1.0,
+                         stream=None):
+    """append(...) then decode_phases(..., phases) in one call; with PHASE_PLAN
+    the plan shares the append's launch."""
+    fn = f"{_PREFIX[cache.fmt]}_append_decode_phases"
+    T = int(k_new.shape[0]) if k_new is not None else 0
+    lay, cd, bd = cache.layout, cache.desc(), batch.desc()
+    st = getattr(load(), fn)(ctypes.byref(lay), ctypes.byref(cd), ctypes.byref(bd), _ptr(k_new), _ptr(v_new),
+                             _ptr(cu_new), T, _ptr(q), float(softmax_scale), _ptr(out), _ptr(lse),
+                             _ptr(workspace), int(workspace.numel()), int(phases), _stream(stream))
     _check(fn, st)
 
 

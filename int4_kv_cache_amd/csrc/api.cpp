@@ -55,17 +55,19 @@ kv4_status cache_batch_check(const kv4_layout* L, const kv4_cache* c, const kv4_
   return KV4_OK;
 }
 
-kv4_status append_impl(int fmt, const kv4_layout* L, const kv4_cache* c, const kv4_batch* b,
-                       const uint16_t* k, const uint16_t* v, const int32_t* cu, int32_t total,
-                       hipStream_t stream) {
+// Checks the append arguments and fills `p`; p.total_new = 0 when there is
+// nothing to append (total 0 or an empty batch).
+kv4_status append_params(int fmt, const kv4_layout* L, const kv4_cache* c, const kv4_batch* b,
+                         const uint16_t* k, const uint16_t* v, const int32_t* cu, int32_t total,
+                         kv4::AppendParams& p) {
   kv4_status s = layout_check(L, fmt);
   if (s != KV4_OK) return s;
   s = cache_batch_check(L, c, b, fmt);
   if (s != KV4_OK) return s;
   if (total < 0) return KV4_ERR_INVALID_ARG;
+  p = kv4::AppendParams{};
   if (total == 0 || b->batch == 0) return KV4_OK;
   if (!k || !v || !cu) return KV4_ERR_INVALID_ARG;
-  kv4::AppendParams p{};
   p.pages = static_cast<uint8_t*>(c->pages);
   p.num_pages = c->num_pages;
   p.side = static_cast<uint8_t*>(c->side);
@@ -88,12 +90,23 @@ kv4_status append_impl(int fmt, const kv4_layout* L, const kv4_cache* c, const k
     p.side = nullptr;
     p.num_slots = 0;
   }
+  return KV4_OK;
+}
+
+kv4_status append_impl(int fmt, const kv4_layout* L, const kv4_cache* c, const kv4_batch* b,
+                       const uint16_t* k, const uint16_t* v, const int32_t* cu, int32_t total,
+                       hipStream_t stream) {
+  kv4::AppendParams p;
+  const kv4_status s = append_params(fmt, L, c, b, k, v, cu, total, p);
+  if (s != KV4_OK || p.total_new == 0) return s;
   return kv4::launch_append(fmt, p, L->head_dim, stream) == hipSuccess ? KV4_OK : KV4_ERR_LAUNCH;
 }
 
-kv4_status decode_impl(int fmt, const kv4_layout* L, const kv4_cache* c, const kv4_batch* b,
-                       const uint16_t* q, float sm, uint16_t* out, float* lse, void* ws, size_t ws_bytes,
-                       unsigned phases, hipStream_t stream, int32_t nq = 1) {
+// Checks the decode arguments and fills `p` and the kernel format `kfmt`.
+// With an empty batch it returns KV4_OK and sets p.batch = 0 (nothing to launch).
+kv4_status decode_params(int fmt, const kv4_layout* L, const kv4_cache* c, const kv4_batch* b,
+                         const uint16_t* q, float sm, uint16_t* out, float* lse, void* ws, size_t ws_bytes,
+                         unsigned phases, int32_t nq, kv4::DecodeParams& p, int& kfmt) {
   if (phases < 1u || phases > 7u) return KV4_ERR_INVALID_ARG;
   if (nq < 1 || nq > KV4_MAX_QUERIES) return KV4_ERR_INVALID_ARG;
   kv4_status s = layout_check(L, fmt);
@@ -107,6 +120,7 @@ kv4_status decode_impl(int fmt, const kv4_layout* L, const kv4_cache* c, const k
     s = cache_batch_check(L, c, b, fmt);
     if (s != KV4_OK) return s;
   }
+  p = kv4::DecodeParams{};
   if (b->batch == 0) return KV4_OK;
   if (!ws) return KV4_ERR_INVALID_ARG;
   if ((phases & (KV4_PHASE_ATTEND | KV4_PHASE_MERGE)) && !out) return KV4_ERR_INVALID_ARG;
@@ -119,7 +133,6 @@ kv4_status decode_impl(int fmt, const kv4_layout* L, const kv4_cache* c, const k
     return KV4_ERR_UNSUPPORTED;
   const size_t need = kv4::decode_workspace_bytes(nv, b->max_pages, L->num_q_heads, L->head_dim);
   if (ws_bytes < need) return KV4_ERR_WORKSPACE;
-  kv4::DecodeParams p{};
   if (c) {
     p.pages = static_cast<const uint8_t*>(c->pages);
     p.num_pages = c->num_pages;
@@ -148,12 +161,37 @@ kv4_status decode_impl(int fmt, const kv4_layout* L, const kv4_cache* c, const k
     p.side = nullptr;
     p.num_slots = 0;
   }
-  int kfmt = fmt;
+  kfmt = fmt;
   if (L->flags & KV4_LAYOUT_INT8_QUERY) {
     if (fmt != kFmtKV4) return KV4_ERR_UNSUPPORTED;
     kfmt = kv4::kFmtKV4Q8;
   }
+  return KV4_OK;
+}
+
+kv4_status decode_impl(int fmt, const kv4_layout* L, const kv4_cache* c, const kv4_batch* b,
+                       const uint16_t* q, float sm, uint16_t* out, float* lse, void* ws, size_t ws_bytes,
+                       unsigned phases, hipStream_t stream, int32_t nq = 1) {
+  kv4::DecodeParams p;
+  int kfmt = fmt;
+  const kv4_status s = decode_params(fmt, L, c, b, q, sm, out, lse, ws, ws_bytes, phases, nq, p, kfmt);
+  if (s != KV4_OK || p.batch == 0) return s;
   return kv4::launch_decode(kfmt, p, L->head_dim, phases, stream) == hipSuccess ? KV4_OK : KV4_ERR_LAUNCH;
+}
+
+// Append, then the selected decode phases; the plan shares the append's launch.
+kv4_status append_decode_impl(int fmt, const kv4_layout* L, const kv4_cache* c, const kv4_batch* b,
+                              const uint16_t* k, const uint16_t* v, const int32_t* cu, int32_t total,
+                              const uint16_t* q, float sm, uint16_t* out, float* lse, void* ws,
+                              size_t ws_bytes, unsigned phases, hipStream_t stream) {
+  kv4::AppendParams a;
+  kv4_status s = append_params(fmt, L, c, b, k, v, cu, total, a);
+  if (s != KV4_OK) return s;
+  kv4::DecodeParams p;
+  int kfmt = fmt;
+  s = decode_params(fmt, L, c, b, q, sm, out, lse, ws, ws_bytes, phases, 1, p, kfmt);
+  if (s != KV4_OK || p.batch == 0) return s;
+  return kv4::launch_decode(kfmt, p, L->head_dim, phases, stream, &a) == hipSuccess ? KV4_OK : KV4_ERR_LAUNCH;
 }
 
 constexpr unsigned kAllPhases = KV4_PHASE_PLAN | KV4_PHASE_ATTEND | KV4_PHASE_MERGE;
@@ -230,6 +268,25 @@ kv4_status kvbf16_decode_phases(const kv4_layout* L, const kv4_cache* c, const k
                                 float sm, uint16_t* out, float* lse, void* ws, size_t ws_bytes, uint32_t phases,
                                 hipStream_t stream) {
   return decode_impl(kFmtBF16, L, c, b, q, sm, out, lse, ws, ws_bytes, phases, stream);
+}
+
+kv4_status kv4_append_decode_phases(const kv4_layout* L, const kv4_cache* c, const kv4_batch* b,
+                                    const uint16_t* k, const uint16_t* v, const int32_t* cu, int32_t total,
+                                    const uint16_t* q, float sm, uint16_t* out, float* lse, void* ws,
+                                    size_t ws_bytes, uint32_t phases, hipStream_t stream) {
+  return append_decode_impl(kFmtKV4, L, c, b, k, v, cu, total, q, sm, out, lse, ws, ws_bytes, phases, stream);
+}
+kv4_status kv8_append_decode_phases(const kv4_layout* L, const kv4_cache* c, const kv4_batch* b,
+                                    const uint16_t* k, const uint16_t* v, const int32_t* cu, int32_t total,
+                                    const uint16_t* q, float sm, uint16_t* out, float* lse, void* ws,
+                                    size_t ws_bytes, uint32_t phases, hipStream_t stream) {
+  return append_decode_impl(kFmtKV8, L, c, b, k, v, cu, total, q, sm, out, lse, ws, ws_bytes, phases, stream);
+}
+kv4_status kvbf16_append_decode_phases(const kv4_layout* L, const kv4_cache* c, const kv4_batch* b,
+                                       const uint16_t* k, const uint16_t* v, const int32_t* cu, int32_t total,
+                                       const uint16_t* q, float sm, uint16_t* out, float* lse, void* ws,
+                                       size_t ws_bytes, uint32_t phases, hipStream_t stream) {
+  return append_decode_impl(kFmtBF16, L, c, b, k, v, cu, total, q, sm, out, lse, ws, ws_bytes, phases, stream);
 }
 
 kv4_status kv4_decode_attention_mq(const kv4_layout* L, const kv4_cache* c, const kv4_batch* b,

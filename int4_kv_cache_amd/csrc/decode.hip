@@ -31,6 +31,7 @@
 // to fp32 rounding.
 #include "kv4_common.h"
 #include "kv4_launch.h"
+#include "append_body.h"
 
 namespace kv4 {
 namespace {
@@ -868,7 +869,7 @@ __device__ inline unsigned long long block_exclusive_scan(unsigned long long v, 
 // plus side tiles), so the units handed out last are the cheapest.  Each
 // thread handles sequences tid, tid + 1024, ...; the first one's lengths
 // are read once and kept.
-__global__ __launch_bounds__(1024) void worklist_kernel(DecodeParams p, int units_per_item) {
+__device__ inline void plan_body(const DecodeParams& p, int units_per_item) {
   __shared__ unsigned long long part[16];
   __shared__ uint32_t bucket[kMaxChunkPages + 2];
   __shared__ uint32_t nmerge;
@@ -953,6 +954,23 @@ __global__ __launch_bounds__(1024) void worklist_kernel(DecodeParams p, int unit
   }
   __syncthreads();
   if (tid == 0) p.ws.header[3] = nmerge;
+}
+
+__global__ __launch_bounds__(1024) void worklist_kernel(DecodeParams p, int units_per_item) {
+  plan_body(p, units_per_item);
+}
+
+// Append and plan in one launch: workgroup 0 writes the work list (it reads
+// only seq_lens, the page table and slot ids, none of which the append
+// writes), the others append one (token, kv head) per wave, so the two
+// latency-bound pieces overlap instead of running one after the other.
+template <int AFMT, int E>
+__global__ __launch_bounds__(1024) void append_plan_kernel(AppendParams a, DecodeParams p, int units_per_item) {
+  if (blockIdx.x == 0) {
+    plan_body(p, units_per_item);
+    return;
+  }
+  append_row<AFMT, E>(a, int64_t(blockIdx.x - 1) * (1024 / kWave) + threadIdx.x / kWave);
 }
 
 // ------------------------------------------------------------- attention --
@@ -1815,7 +1833,7 @@ int device_cus() {
 }
 
 template <int FMT, int D>
-hipError_t launch_fd(DecodeParams p, unsigned phases, hipStream_t stream) {
+hipError_t launch_fd(DecodeParams p, unsigned phases, const AppendParams* append, hipStream_t stream) {
   constexpr int HB = 16 / (D / 32);
   const int cus = device_cus();
   if (cus <= 0) return hipErrorInvalidDevice;
@@ -1829,8 +1847,19 @@ hipError_t launch_fd(DecodeParams p, unsigned phases, hipStream_t stream) {
   p.resident_waves = blocks * (kAttnThreads / kWave);
   if (phases & 1u) {
     const int units_per_item = mc ? p.num_kv_heads : p.num_kv_heads * ((G + HB - 1) / HB);
-    hipLaunchKernelGGL(worklist_kernel, dim3(1), dim3(1024), 0, stream, p, units_per_item);
+    if (append && append->total_new > 0) {
+      constexpr int AFMT = FMT == kFmtKV4Q8 ? kFmtKV4 : FMT;
+      const int64_t waves = int64_t(append->total_new) * append->num_kv_heads;
+      const unsigned blocks_a = unsigned(1 + (waves + 1024 / kWave - 1) / (1024 / kWave));
+      hipLaunchKernelGGL((append_plan_kernel<AFMT, D / kWave>), dim3(blocks_a), dim3(1024), 0, stream, *append, p,
+                         units_per_item);
+    } else {
+      hipLaunchKernelGGL(worklist_kernel, dim3(1), dim3(1024), 0, stream, p, units_per_item);
+    }
     const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  } else if (append && append->total_new > 0) {
+    const hipError_t err = launch_append(FMT == kFmtKV4Q8 ? kFmtKV4 : FMT, *append, D, stream);
     if (err != hipSuccess) return err;
   }
   if (phases & 2u) {
@@ -1851,8 +1880,10 @@ hipError_t launch_fd(DecodeParams p, unsigned phases, hipStream_t stream) {
 }
 
 template <int FMT>
-hipError_t launch_fmt(const DecodeParams& p, int head_dim, unsigned phases, hipStream_t stream) {
-  return head_dim == 128 ? launch_fd<FMT, 128>(p, phases, stream) : launch_fd<FMT, 64>(p, phases, stream);
+hipError_t launch_fmt(const DecodeParams& p, int head_dim, unsigned phases, const AppendParams* append,
+                      hipStream_t stream) {
+  return head_dim == 128 ? launch_fd<FMT, 128>(p, phases, append, stream)
+                         : launch_fd<FMT, 64>(p, phases, append, stream);
 }
 
 }  // namespace
@@ -1904,11 +1935,12 @@ DecodeWorkspace carve_workspace(void* base, int32_t batch, int32_t max_pages, in
   return w;
 }
 
-hipError_t launch_decode(int fmt, const DecodeParams& p, int head_dim, unsigned phases, hipStream_t stream) {
-  if (fmt == kFmtKV4) return launch_fmt<kFmtKV4>(p, head_dim, phases, stream);
-  if (fmt == kFmtKV4Q8) return launch_fmt<kFmtKV4Q8>(p, head_dim, phases, stream);
-  if (fmt == kFmtKV8) return launch_fmt<kFmtKV8>(p, head_dim, phases, stream);
-  return launch_fmt<kFmtBF16>(p, head_dim, phases, stream);
+hipError_t launch_decode(int fmt, const DecodeParams& p, int head_dim, unsigned phases, hipStream_t stream,
+                         const AppendParams* append) {
+  if (fmt == kFmtKV4) return launch_fmt<kFmtKV4>(p, head_dim, phases, append, stream);
+  if (fmt == kFmtKV4Q8) return launch_fmt<kFmtKV4Q8>(p, head_dim, phases, append, stream);
+  if (fmt == kFmtKV8) return launch_fmt<kFmtKV8>(p, head_dim, phases, append, stream);
+  return launch_fmt<kFmtBF16>(p, head_dim, phases, append, stream);
 }
 
 }  // namespace kv4

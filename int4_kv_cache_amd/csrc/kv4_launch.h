@@ -75,7 +75,10 @@ bool decode_units_fit(int32_t batch, int32_t max_pages, int32_t num_q_heads, int
 DecodeWorkspace carve_workspace(void* base, int32_t batch, int32_t max_pages, int32_t num_q_heads,
                                 int32_t head_dim);
 // phases: bit 0 work list, bit 1 attention, bit 2 merge
-hipError_t launch_decode(int fmt, const DecodeParams& p, int head_dim, unsigned phases, hipStream_t stream);
+// `append` (optional): new tokens stored before the decode phases run, in the
+// same launch as the plan when `phases` holds it.
+hipError_t launch_decode(int fmt, const DecodeParams& p, int head_dim, unsigned phases, hipStream_t stream,
+                         const AppendParams* append = nullptr);
 
 hipError_t launch_probe(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream);
 int32_t probe_blocks();

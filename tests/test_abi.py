@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.kv4_abi_version() == 3
+    assert lib.kv4_abi_version() == 4
     for code, text in kv4.STATUS.items():
         assert lib.kv4_status_string(code).decode() == text
     assert lib.kv4_status_string(12345).decode() == "unknown status"
@@ -147,6 +147,21 @@ def test_host_argument_errors_return_before_launch(lib):
                                  None, None, fake, 1 << 40, 4, None) == -1      # merge needs out
     assert lib.kv8_decode_phases(ctypes.byref(good), None, ctypes.byref(kv4.BatchDesc(fake, 4, fake, None, 0)),
                                  None, 1.0, None, None, None, 0, 1, None) == 0  # empty batch
+    # append + decode in one call: both calls' checks, before any launch
+    def fused(lay=good, c=cache, b=batch, k=fake, total=3, q=fake, out=fake, ws_bytes=1 << 40, ph=7):
+        return lib.kv4_append_decode_phases(ctypes.byref(lay), None if c is None else ctypes.byref(c),
+                                            ctypes.byref(b), k, fake, fake, total, q, 1.0, out, None, fake,
+                                            ws_bytes, ph, None)
+    assert fused(lay=kv4.make_layout(32, 8, 96, 16, 128)) == -2     # layout (append check)
+    assert fused(k=None) == -1                                       # append needs k_new
+    assert fused(total=-1) == -1
+    assert fused(ph=0) == -1 and fused(ph=8) == -1                   # decode check
+    assert fused(q=None) == -1 and fused(out=None) == -1
+    assert fused(ws_bytes=16) == -3
+    assert fused(c=None, ph=1) == -1                                 # the cache is required even for a plan
+    assert fused(b=kv4.BatchDesc(fake, 4, fake, None, 0)) == 0       # empty batch: nothing to do
+    assert lib.kv8_append_decode_phases(ctypes.byref(good), ctypes.byref(cache), ctypes.byref(batch), fake, fake,
+                                        fake, 3, fake, 1.0, fake, None, fake, 16, 7, None) == -3
     # probe
     assert lib.kv4_hbm_read_probe(fake, 17, fake, None) == -1
     assert lib.kv4_hbm_read_probe(None, 16, fake, None) == -1
