@@ -55,6 +55,9 @@ typedef uint32_t u32x4_t __attribute__((__vector_size__(16)));
 #ifndef KV4_UNITS_PER_WAVE
 #define KV4_UNITS_PER_WAVE 8  // work-list granularity: chunk size from the total work
 #endif
+#ifndef KV4_MERGE_K
+#define KV4_MERGE_K 4  // partial rows a merge task loads per round (8: 104 registers, 0.85 us slower)
+#endif
 #ifndef KV4_STAGES8
 #define KV4_STAGES8 2  // pipeline depth of the INT8 tile loops
 #endif
@@ -1748,7 +1751,7 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeParams p) {
   // of a wave proceed independently.
   constexpr int QL = 16;      // lanes per task
   constexpr int E = D / QL;   // channels per lane
-  constexpr int K = 8;        // items per round
+  constexpr int K = KV4_MERGE_K;  // items per round
   constexpr int RS = part_stride(D);
   const int sub = threadIdx.x & (QL - 1);
   const int Hq = p.num_q_heads;
