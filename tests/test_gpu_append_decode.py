@@ -95,3 +95,40 @@ def test_fused_matches_separate_calls(kv4, fmt, q8):
     assert torch.equal(out.view(torch.int16), ref_out.view(torch.int16))
     assert torch.equal(lse.view(torch.int32), ref_lse.view(torch.int32))
     assert torch.equal(wl.cache.pages, before[0])
+
+
+@pytest.mark.parametrize("fmt", [0, 1], ids=["kv4", "kv8"])
+def test_fused_multi_token_reappend(kv4, fmt):
+    """Several tokens per sequence in one fused call: the last three positions
+    of every sequence appended again (host-built cache, so the tokens are
+    known) leave every page and side byte unchanged, and the decode matches
+    the separate decode bit for bit."""
+    import torch
+
+    from harness import build_from_host
+    from harness.device import _bf16, _i32
+
+    wl = build_from_host(0, fmt)
+    wl.decode()
+    torch.cuda.synchronize()
+    ref_out, ref_lse = wl.out.clone(), wl.lse.clone()
+    pages = wl.cache.pages.clone()
+    side = wl.cache.side.clone() if getattr(wl.cache, "side", None) is not None else None
+    n_b = np.minimum(wl.lengths, 3)
+    ks = [wl.tokens["host_k"][b][wl.lengths[b] - n_b[b]:] for b in range(wl.lengths.size)]
+    vs = [wl.tokens["host_v"][b][wl.lengths[b] - n_b[b]:] for b in range(wl.lengths.size)]
+    k_new = _bf16(np.concatenate(ks), "cuda")
+    v_new = _bf16(np.concatenate(vs), "cuda")
+    cu = _i32(np.concatenate([[0], np.cumsum(n_b)]), "cuda")
+    print(f"\nre-append {int(n_b.sum())} tokens over {wl.lengths.size} sequences, fmt={fmt}", flush=True)
+    out = torch.full_like(wl.out, float("nan"))
+    lse = torch.full_like(wl.lse, float("nan"))
+    ws = torch.empty_like(wl.workspace)
+    ws.fill_(0x33)
+    kv4.append_decode_phases(wl.cache, wl.batch, k_new, v_new, cu, wl.q, out, lse, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(wl.cache.pages, pages)
+    if side is not None:
+        assert torch.equal(wl.cache.side, side)
+    assert torch.equal(out.view(torch.int16), ref_out.view(torch.int16))
+    assert torch.equal(lse.view(torch.int32), ref_lse.view(torch.int32))
