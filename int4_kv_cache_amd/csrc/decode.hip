@@ -488,8 +488,7 @@ __device__ inline void step(Unit<D>& u, const Tile<KIND, D>& T0, const Tile<KIND
       z1 = ((va1 >> g) & 1u) ? z1 : -INFINITY;
     }
     float mx = fmaxf(z0, z1);
-    float r = 1.0f;
-    if (__any(mx * sc > u.m + kRescale)) {
+    if (__any(mx * sc > u.m + kRescale)) {  // wave-uniform, rare
       mx = fmaxf(mx, quad_xor1(mx));
       mx = fmaxf(mx, quad_xor2(mx));
       mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
@@ -498,12 +497,14 @@ __device__ inline void step(Unit<D>& u, const Tile<KIND, D>& T0, const Tile<KIND
       const float alpha = (mn == u.m) ? 1.0f : __builtin_amdgcn_exp2f(u.m - mn);
       u.l *= alpha;
       u.m = mn;
-      r = head_value_for_acc<D>(alpha, lane, 0);
+      // only the accumulator element of each N-tile that holds the head's
+      // own group is used (the others are discarded at the end)
+      const float r = head_value_for_acc<D>(alpha, lane, 0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) u.corr[e] *= r;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) u.o[t][t / 2] *= r;
     }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) u.corr[e] *= r;
-#pragma unroll
-    for (int t = 0; t < NT; ++t) u.o[t][t / 2] *= r;
     const float mneg = u.m == -INFINITY ? 0.0f : -u.m;
     const float p0 = __builtin_amdgcn_exp2f(fmaf(z0, sc, mneg));
     const float p1 = __builtin_amdgcn_exp2f(fmaf(z1, sc, mneg));
