@@ -53,10 +53,13 @@ typedef uint32_t u32x4_t __attribute__((__vector_size__(16)));
 #define KV4_MC_STAGES 1  // pipeline depth of the multi-column kernel (2 measured 1.3% slower)
 #endif
 #ifndef KV4_UNITS_PER_WAVE
-#define KV4_UNITS_PER_WAVE 8  // work-list granularity: chunk size from the total work
+#define KV4_UNITS_PER_WAVE 6  // work-list granularity: chunk size from the total work
 #endif
 #ifndef KV4_MERGE_K
 #define KV4_MERGE_K 4  // partial rows a merge task loads per round (8: 104 registers, 0.85 us slower)
+#endif
+#ifndef KV4_MAX_CHUNK
+#define KV4_MAX_CHUNK 128  // largest chunk of the single-query kernel (two page ids per lane)
 #endif
 #ifndef KV4_STAGES8
 #define KV4_STAGES8 2  // pipeline depth of the INT8 tile loops
@@ -760,7 +763,9 @@ __device__ inline uint32_t range_mask(int lo, int hi) {  // bits [lo, hi) of 0..
 }
 
 // ---------------------------------------------------------------- worklist --
-constexpr int kMaxChunkPages = 64;  // one lane per page id of an item
+constexpr int kMaxChunkPages = KV4_MAX_CHUNK;  // two page ids per lane in the single-query kernel
+constexpr int kMaxChunkPagesMc = 64;           // one page id per lane in the multi-column kernel
+static_assert(kMaxChunkPages == 64 || kMaxChunkPages == 128, "one or two page ids per lane");
 constexpr int kProtectedCost = 2;    // an INT8 tile costs about two INT4 pages
 
 struct SeqWork {
@@ -893,7 +898,8 @@ __device__ inline void plan_body(const DecodeParams& p, int units_per_item) {
   // about KV4_UNITS_PER_WAVE units per resident wave
   const unsigned long long denom = unsigned(KV4_UNITS_PER_WAVE) * unsigned(p.resident_waves > 0 ? p.resident_waves : 1);
   unsigned long long cl = (total_pages * unsigned(units_per_item) + denom - 1) / denom;
-  cl = cl < unsigned(kChunkPages) ? unsigned(kChunkPages) : (cl > unsigned(kMaxChunkPages) ? kMaxChunkPages : cl);
+  const unsigned cmax = p.tq > 1 ? unsigned(kMaxChunkPagesMc) : unsigned(kMaxChunkPages);
+  cl = cl < unsigned(kChunkPages) ? unsigned(kChunkPages) : (cl > cmax ? cmax : cl);
   const int chunk = int(cl);
 
   // pass 1: full items (scan) and the histogram of the other items' sizes
@@ -924,12 +930,22 @@ __device__ inline void plan_body(const DecodeParams& p, int units_per_item) {
   // positions of the shorter items, costliest first (bucket i holds key
   // kMaxChunkPages - i): an exclusive scan of the bucket counts by wave 0
   if (wid == 0) {
-    const int i0 = 2 * lane, i1 = 2 * lane + 1;
-    const uint32_t c0 = i0 <= kMaxChunkPages ? bucket[i0] : 0u, c1 = i1 <= kMaxChunkPages ? bucket[i1] : 0u;
-    const unsigned long long inc = wave_scan_u64((unsigned long long)(c0 + c1), lane);
-    const uint32_t start = uint32_t(run_full) + uint32_t(inc) - (c0 + c1);
-    if (i0 <= kMaxChunkPages) bucket[i0] = start;
-    if (i1 <= kMaxChunkPages) bucket[i1] = start + c0;
+    constexpr int BPL = (kMaxChunkPages + kWave) / kWave;  // buckets per lane (kMaxChunkPages + 1 of them)
+    uint32_t c[BPL], sum = 0u;
+#pragma unroll
+    for (int k = 0; k < BPL; ++k) {
+      const int i = BPL * lane + k;
+      c[k] = i <= kMaxChunkPages ? bucket[i] : 0u;
+      sum += c[k];
+    }
+    const unsigned long long inc = wave_scan_u64((unsigned long long)sum, lane);
+    uint32_t start = uint32_t(run_full) + uint32_t(inc) - sum;
+#pragma unroll
+    for (int k = 0; k < BPL; ++k) {
+      const int i = BPL * lane + k;
+      if (i <= kMaxChunkPages) bucket[i] = start;
+      start += c[k];
+    }
     if (lane == kWave - 1) {
       p.ws.header[0] = 0u;
       p.ws.header[1] = uint32_t(run_full) + uint32_t(inc);
@@ -1066,29 +1082,39 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(KV
   // and every check is made when the unit starts, so nothing waits for them
   // early.  A page is shared when a neighbour holds the same physical page at
   // the same index: a shared prompt.
+  // With 128-page chunks a lane holds pages lane and lane + 64 of the item.
+  constexpr int NH = kMaxChunkPages / kWave;  // page ids per lane
   struct Pids {
-    int x, xp, xn;
+    int x[NH], xp[NH], xn[NH];
   };
   auto fetch_pids = [&](const ItemDesc& d) -> Pids {
-    const int col = d.first + lane < p.max_pages ? d.first + lane : p.max_pages - 1;
     const int nv = p.batch * p.nq;
     const int bp = d.b > 0 ? d.b - 1 : 0, bn = d.b + 1 < nv ? d.b + 1 : d.b;
     Pids r;
-    r.x = p.page_table[int64_t(d.b / p.nq) * p.max_pages + col];  // tq = 1: u = b * nq + t
-    r.xp = r.xn = -1;
-    if constexpr (KV4 && KV4_NT_LOADS) {
-      r.xp = p.page_table[int64_t(bp / p.nq) * p.max_pages + col];
-      r.xn = p.page_table[int64_t(bn / p.nq) * p.max_pages + col];
+#pragma unroll
+    for (int k = 0; k < NH; ++k) {
+      const int c = d.first + lane + k * kWave;
+      const int col = c < p.max_pages ? c : p.max_pages - 1;
+      r.x[k] = p.page_table[int64_t(d.b / p.nq) * p.max_pages + col];  // tq = 1: u = b * nq + t
+      r.xp[k] = r.xn[k] = -1;
+      if constexpr (KV4 && KV4_NT_LOADS) {
+        r.xp[k] = p.page_table[int64_t(bp / p.nq) * p.max_pages + col];
+        r.xn[k] = p.page_table[int64_t(bn / p.nq) * p.max_pages + col];
+      }
     }
     return r;
   };
-  // this lane's page id (-1 past the item or out of range) and the lane mask
-  // of shared pages
-  auto resolve_pids = [&](const Pids& r, const ItemDesc& d, int& pid, uint64_t& shared) {
-    const bool ok = lane < d.npg && r.x >= 0 && int64_t(r.x) < p.num_pages;
-    pid = ok ? r.x : -1;
-    const bool sh = ok && ((d.b > 0 && r.xp == r.x) || (d.b + 1 < p.batch * p.nq && r.xn == r.x));
-    shared = __ballot(KV4 && KV4_NT_LOADS && sh);
+  // this lane's page ids (-1 past the item or out of range) and the lane
+  // masks of shared pages, one per half
+  auto resolve_pids = [&](const Pids& r, const ItemDesc& d, int (&pid)[NH], uint64_t (&shared)[NH]) {
+#pragma unroll
+    for (int k = 0; k < NH; ++k) {
+      const bool ok = lane + k * kWave < d.npg && r.x[k] >= 0 && int64_t(r.x[k]) < p.num_pages;
+      pid[k] = ok ? r.x[k] : -1;
+      const bool sh =
+          ok && ((d.b > 0 && r.xp[k] == r.x[k]) || (d.b + 1 < p.batch * p.nq && r.xn[k] == r.x[k]));
+      shared[k] = __ballot(KV4 && KV4_NT_LOADS && sh);
+    }
   };
   uint32_t t0 = grab();
   uint32_t t1 = grab();
@@ -1098,8 +1124,8 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(KV
 
   while (t0 < units) {
     // this unit's page ids (loaded during the previous unit)
-    int pid0v;
-    uint64_t shared0;
+    int pid0v[NH];
+    uint64_t shared0[NH];
     resolve_pids(pid0, d0, pid0v, shared0);
     // ---- run-ahead for the following units (fixed position, unconditional)
     const uint32_t t2 = grab();
@@ -1230,24 +1256,33 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(KV
       run_tiles<kInt8Tile, D, KV4_STAGES8, Q8, false>(u, ntiles, ptr, mask, lane, setup);
     }
 
-    // ---- middle pages of this item (at most 64: one page id per lane)
+    // ---- middle pages of this item (at most kMaxChunkPages: NH page ids per lane)
     if (d.npg > 0) {
       constexpr int ST = MAIN == kInt4Page ? KV4_STAGES : (MAIN == kInt8Tile ? KV4_STAGES8 : 1);
       // pages [0, ns) of the item are shared with a neighbouring sequence
-      const int ns = ~shared0 == 0ull ? kWave : int(__builtin_ctzll(~shared0));
+      int ns = ~shared0[0] == 0ull ? kWave : int(__builtin_ctzll(~shared0[0]));
+      if constexpr (NH == 2) {
+        if (ns == kWave) ns += ~shared0[1] == 0ull ? kWave : int(__builtin_ctzll(~shared0[1]));
+      }
       auto ptr = [&](int i) {
-        const int pid = __builtin_amdgcn_readlane(pid0v, i);
+        int pid = __builtin_amdgcn_readlane(pid0v[0], i & (kWave - 1));
+        if constexpr (NH == 2) {
+          if (i >= kWave) pid = __builtin_amdgcn_readlane(pid0v[1], i & (kWave - 1));
+        }
         return p.pages + (int64_t(pid < 0 ? 0 : pid) * H + h) * p.block_bytes;
       };
       // Row masks: the region [mb, me) can cut only the item's first and last
       // pages; a page whose id is out of range contributes nothing.
-      const uint64_t okm = __ballot(pid0v >= 0);
+      uint64_t okmv[NH];
+#pragma unroll
+      for (int k = 0; k < NH; ++k) okmv[k] = __ballot(pid0v[k] >= 0);
       const int pf = d.first * kPage, il = d.npg - 1;
       const uint32_t m_first = range_mask(g.mb - pf, g.me - pf);
       const uint32_t m_last = range_mask(g.mb - pf - il * kPage, g.me - pf - il * kPage);
       auto mask = [&](int i) {
         const uint32_t m = i == 0 ? m_first : (i == il ? m_last : 0xFFFFu);
-        return ((okm >> i) & 1ull) ? m : 0u;
+        const uint64_t okm = (NH == 2 && i >= kWave) ? okmv[NH - 1] : okmv[0];
+        return ((okm >> (i & (kWave - 1))) & 1ull) ? m : 0u;
       };
       if constexpr (MAIN == kInt4Page && KV4_NT_LOADS) {
         run_tiles<MAIN, D, ST, Q8, false>(u, ns, ptr, mask, lane, setup);
