@@ -130,6 +130,30 @@ def test_golden_quantizer_cases_on_gpu(kv4):
         assert int(got[off]) | (int(got[off + 1]) << 8) == c["scale"], c["id"]
 
 
+def test_golden_layout_cases_on_gpu(kv4):
+    """The hand-worked byte-layout cases (K and V codes and scales of INT4
+    pages, INT8 pages, the INT8 side tile and bf16 pages), appended by the GPU."""
+    import torch
+
+    import int4_kv_cache_amd as lib
+    from test_oracle_layout_golden import CASES, case_inputs, expected_buffer
+
+    i32 = lambda a: torch.as_tensor(np.asarray(a, np.int32), device="cuda")
+    for c in CASES:
+        fmt = {0: lib.FMT_KV4, 1: lib.FMT_KV8, 2: lib.FMT_BF16}[c["fmt"]]
+        lay = lib.make_layout(1, 1, c["D"], c["S"], c["R"])
+        cache = lib.alloc_cache(fmt, lay, 1, 1)
+        k, v = case_inputs(c)
+        kt = torch.as_tensor(k.view(np.int16), device="cuda").view(torch.bfloat16)
+        vt = torch.as_tensor(v.view(np.int16), device="cuda").view(torch.bfloat16)
+        lib.append(cache, lib.Batch(i32([[0]]), i32([16])), kt, vt, i32([0, 16]))
+        buf = cache.pages if c["area"] == "page" else cache.side
+        got = buf.cpu().numpy()
+        want = expected_buffer(c, got.size)
+        bad = np.flatnonzero(got != want)
+        assert bad.size == 0, f"{c['id']}: bytes differ at {bad[:8].tolist()}"
+
+
 def test_config1_sampled(kv4):
     from harness import build_config
 
