@@ -17,7 +17,7 @@ bytes; `traffic` is the HBM bytes per launch from the committed rocprofv3
 counter runs (null once the kernel sources differ from the ones measured).
 `cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--variants] [--no-cpu]
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-variants] [--no-cpu] [--mq T]
 """
 from __future__ import annotations
 
@@ -116,84 +116,111 @@ def measured_traffic():
     return rec.get("bytes_per_launch")
 
 
-def time_steps(wl, steps, warmup, append=True):
-    """Time `steps` decode steps after `warmup` untimed ones.
+def settle(step, min_s=2.0, max_s=12.0, window=100):
+    """Run `step` in windows of `window` calls, timed with HIP events, until at
+    least `min_s` seconds have passed and two windows in a row agree within
+    1%, or `max_s` seconds.  The GPU raises its clocks over the first second
+    or so of sustained load (a timed region that starts on a cold GPU ran the
+    attention kernel about 10% slower), so this runs before the requested
+    warm-up steps whatever their number.  Returns (calls, seconds, last
+    window's ms per call)."""
+    import torch
 
-    A step is the append of one token per sequence (if `append`) and the
-    decode as its three phases (plan, attend, merge) on one stream: with an
-    append, kv4_append_decode_phases stores the tokens and makes the plan in
-    one launch, then kv4_decode_phases runs ATTEND and MERGE.  In the timed
-    region only the attention launch is bracketed by HIP events on that
-    stream: every event record costs the stream 2-3 us, so the phases are
-    timed in a second pass of the same steps with an event between every
-    phase (there the append and the plan run as separate launches, to show
-    each).  Returns the mean ms per step over the timed region, and per-step
-    ms arrays of every phase (attend from the timed region, the rest and
-    "step_with_phase_events" from the second pass).
+    stream = torch.cuda.current_stream()
+    t0 = time.perf_counter()
+    calls, prev, last = 0, None, None
+    while True:
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(window):
+            step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        calls += window
+        last = e0.elapsed_time(e1) / window
+        el = time.perf_counter() - t0
+        if el >= max_s or (el >= min_s and prev is not None and abs(last - prev) <= 0.01 * prev):
+            return calls, el, last
+        prev = last
+
+
+def time_steps(wl, steps, warmup, settle_s=2.0):
+    """Time `steps` decode steps after the clock-settling run and `warmup`
+    untimed steps.
+
+    A step is GpuWorkload.step_launches(): the append of one token per
+    sequence with the plan in the same launch (kv4_append_decode_phases), then
+    ATTEND, then MERGE, on one stream.  In the timed region only the attention
+    launch is bracketed by HIP events on that stream (every event record
+    costs the stream 2-3 us).  A second pass of the same steps puts an event
+    between every launch; every per-phase figure comes from that pass.
+    Returns (mean ms per step of the timed region, attend ms per step of the
+    timed region, per-phase ms arrays of the second pass, settle record).
     """
     import torch
 
-    import int4_kv_cache_amd as kv4
-
     stream = torch.cuda.current_stream()
+    launches = wl.step_launches()
 
-    def phase(mask):
-        kv4.decode_phases(wl.cache, wl.batch, wl.q, wl.out, wl.lse, wl.workspace, mask)
+    def step():
+        for launch in launches:
+            launch()
 
-    def new_events(n, k):
-        return [[torch.cuda.Event(enable_timing=True) for _ in range(k)] for _ in range(n)]
-
+    n_settle, s_settle, ms_settle = settle(step, min_s=settle_s)
     for _ in range(warmup):
-        if append:
-            wl.step_append()
-        wl.decode()
+        step()
     torch.cuda.synchronize()
-    ev = new_events(steps, 2)
+    plan, attend, merge = launches
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0.record(stream)
     for e in ev:
-        if append:
-            kv4.append_decode_phases(wl.cache, wl.batch, wl.step_k, wl.step_v, wl.step_cu, wl.q, wl.out, wl.lse,
-                                     wl.workspace, kv4.PHASE_PLAN)
-        else:
-            phase(kv4.PHASE_PLAN)
+        plan()
         e[0].record(stream)
-        phase(kv4.PHASE_ATTEND)
+        attend()
         e[1].record(stream)
-        phase(kv4.PHASE_MERGE)
+        merge()
     t1.record(stream)
     torch.cuda.synchronize()
     total_ms = t0.elapsed_time(t1)
-    attend = np.array([e[0].elapsed_time(e[1]) for e in ev])
-    # breakdown pass (not the timed region)
-    ev = new_events(steps, 5)
+    att = np.array([e[0].elapsed_time(e[1]) for e in ev])
+    # phase pass: an event between every launch
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
     for e in ev:
         e[0].record(stream)
-        if append:
-            wl.step_append()
+        plan()
         e[1].record(stream)
-        phase(kv4.PHASE_PLAN)
+        attend()
         e[2].record(stream)
-        phase(kv4.PHASE_ATTEND)
+        merge()
         e[3].record(stream)
-        phase(kv4.PHASE_MERGE)
-        e[4].record(stream)
     torch.cuda.synchronize()
     ph = {name: np.array([e[i].elapsed_time(e[i + 1]) for e in ev])
-          for i, name in enumerate(("append", "plan", "attend_breakdown", "merge"))}
-    ph["attend"] = attend
-    ph["decode"] = ph["plan"] + ph["attend"] + ph["merge"]
-    ph["step_with_phase_events"] = np.array([e[0].elapsed_time(e[4]) for e in ev])
-    return total_ms / steps, ph
+          for i, name in enumerate(("append_plan", "attend", "merge"))}
+    ph["step"] = np.array([e[0].elapsed_time(e[3]) for e in ev])
+    return total_ms / steps, att, ph, {"steps": n_settle, "s": round(s_settle, 2),
+                                       "last_window_ms_per_step": ms_settle}
 
 
-def time_multi_query(wl, T, steps, warmup, decode_bytes, decode_us):
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def time_multi_query(wl, T, steps, warmup, decode_bytes, step_us):
     """kv4_decode_attention_mq with T query tokens per sequence over the
-    workload's cache as it stands (the last T positions are the queries).
-    Algorithmic bytes: the single-token decode's (every cache byte once) plus
-    the q / out / lse of the T - 1 extra queries."""
+    workload's cache as it stands (the last T positions are the queries),
+    timed with HIP events around each call (plan + attend + merge; the
+    attention kernel is all but a few tens of microseconds of it).
+
+    Two rooflines.  HBM: the single-token decode's algorithmic bytes (every
+    cache byte once) plus the q / out / lse of the T - 1 extra queries.
+    Matrix cores: the useful flops, 4 * head_dim per (query, query head,
+    position it sees) -- 2 * D for q.k and 2 * D for p.v -- against the
+    2.5 PFLOP/s dense bf16 peak.  The multi-column kernel is bound by neither:
+    it is bound by instruction issue (conversions, scales and the softmax on
+    the vector ALU next to the MFMAs), so both fractions are low."""
     import torch
 
     import int4_kv_cache_amd as kv4
@@ -214,21 +241,28 @@ def time_multi_query(wl, T, steps, warmup, decode_bytes, decode_us):
     for _ in range(warmup):
         call()
     torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(steps):
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for e in ev:
+        e[0].record(stream)
         call()
-    e1.record(stream)
+        e[1].record(stream)
     torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) / steps * 1e3
+    per = np.array([e[0].elapsed_time(e[1]) for e in ev]) * 1e3
+    us = float(per.mean())
     extra = (T - 1) * B * cfg.num_q_heads * (cfg.head_dim * 4 + 4)
     nbytes = decode_bytes + extra
+    L = wl.lengths.astype(np.int64)
+    seen = sum(np.maximum(L - T + t + 1, 0).sum() for t in range(T))
+    flops = float(seen) * cfg.num_q_heads * 4 * cfg.head_dim
+    tflops = flops / (us * 1e-6) / 1e12
     del q, out, lse, ws
     torch.cuda.empty_cache()
-    return {"T": T, "us": us, "query_tokens_per_s": B * T / (us * 1e-6),
+    return {"T": T, "us": us, "us_min": float(per.min()), "query_tokens_per_s": B * T / (us * 1e-6),
             "hbm_frac": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, "algorithmic_bytes": int(nbytes),
-            "vs_T_single_token_decodes": us / (T * decode_us),
+            "roofline_mfma": {"bound": "issue", "achieved": tflops, "peak": MFMA_BF16_PEAK_TFLOPS,
+                              "unit": "TFLOP/s", "frac": tflops / MFMA_BF16_PEAK_TFLOPS,
+                              "algorithmic_flops": flops},
+            "vs_T_single_token_steps": us / (T * step_us),
             "note": "plan + attend + merge; at head_dim 128 on INT4 pages one unit serves 16 / G "
                     "queries (the multi-column kernel), otherwise each query reads the cache itself"}
 
@@ -253,14 +287,16 @@ def capacity(budget_gb=240.0, layers=36, repeats=64):
             "sequences": out, "vs_bf16": {k: out[k] / out["bf16"] for k in out}}
 
 
-def cpu_baseline(wl, budget_s=12.0, max_seqs=256):
-    """The oracle, untuned, on a bounded sample of the same workload."""
+def cpu_baseline(wl, budget_s=12.0, max_seqs=256, threads=None):
+    """The oracle, untuned, on a bounded sample of the same workload, with
+    `threads` OpenMP threads (default: OMP_NUM_THREADS, else every core)."""
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     import oracle
     import parity_util as pu
 
     oracle.build(force=False)
-    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    if threads is None:
+        threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     rng = np.random.default_rng(123)
     order = rng.permutation(wl.lengths.size)
     n = 8
@@ -416,8 +452,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--variants", action="store_true",
-                    help="also time kv8 / bf16 / plain INT4 / KV4 with the integer query")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the bf16 / kv8 / plain INT4 / integer-query variants on the same workload")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--config", type=int, default=CFG_IDX, choices=(2, 3),
                     help="2: one Qwen3-8B-shaped layer, B=1024 (the default line); 3: the 36-layer "
@@ -449,9 +485,9 @@ def main():
     wl = build_config(CFG_IDX, kv4.FMT_KV4, keep_inputs=not args.no_cpu)
     ctx = int(wl.lengths.sum())
     print(f"[bench] built: batch {wl.lengths.size}, ctx tokens {ctx}", file=sys.stderr, flush=True)
-    ms, ph = time_steps(wl, args.steps, args.warmup)
+    ms, att, ph, settled = time_steps(wl, args.steps, args.warmup)
     abytes = algorithmic_bytes(wl, 0)
-    att_ms = float(np.mean(ph["attend"]))
+    att_ms = float(np.mean(att))
     achieved = attend_bytes(wl, 0) / (att_ms * 1e-3) / 1e9
     us = {k: float(np.mean(v)) * 1e3 for k, v in ph.items()}
     result = {
@@ -471,12 +507,17 @@ def main():
                                "prompt), lognormal responses mean 2k cap 16384, Hq 32 / Hkv 8 / D 128, "
                                "16 sinks + 128 recent INT8; step = append 1 token/seq + decode",
                    "global_batch": int(wl.lengths.size), "ctx_tokens": ctx,
-                   "append_us": us["append"], "plan_us": us["plan"], "attend_us": us["attend"],
-                   "merge_us": us["merge"], "decode_us": us["decode"],
-                   "step_us_with_phase_events": us["step_with_phase_events"],
-                   "decode_us_median": float(np.median(ph["decode"])) * 1e3,
-                   "decode_hbm_frac": abytes / (us["decode"] * 1e-6) / 1e9 / HBM_PEAK_GBS,
-                   "decode_algorithmic_bytes": abytes},
+                   "attend_us": att_ms * 1e3,
+                   "attend_us_per_step": [round(float(x) * 1e3, 1) for x in att],
+                   "attend_us_median": float(np.median(att)) * 1e3,
+                   "phases_us": {"append_plan": us["append_plan"], "attend": us["attend"],
+                                 "merge": us["merge"], "step": us["step"],
+                                 "note": "one pass with an event between every launch (each record costs "
+                                         "2-3 us); append_plan is the append of the step tokens with the "
+                                         "plan in the same launch"},
+                   "step_hbm_frac": abytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                   "decode_algorithmic_bytes": abytes,
+                   "settle": dict(settled, note="clock-settling steps run before the warm-up steps")},
         "hbm_read_probe_gbs": read_probe_gbs(),
         "capacity": capacity(),
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -484,28 +525,36 @@ def main():
                      "kernel": "attention_kernel<kv4, 128> (the ATTEND phase)",
                      "algorithmic_bytes": attend_bytes(wl, 0)},
     }
-    if args.variants:
+    if not args.no_variants:
+        # the reference kernels and plain INT4 on the same seeded workload
+        # (config 4's formats), each timed like the KV4-RL step
         var = {}
-        for fmt, name, S, R, q8 in ((kv4.FMT_KV8, "kv8", 0, 0, False), (kv4.FMT_BF16, "bf16", 0, 0, False),
+        for fmt, name, S, R, q8 in ((kv4.FMT_BF16, "bf16", 0, 0, False), (kv4.FMT_KV8, "kv8", 0, 0, False),
                                     (kv4.FMT_KV4, "int4_plain", 0, 0, False),
                                     (kv4.FMT_KV4, "kv4_rl_int8_query", None, None, True)):
+            print(f"[bench] variant {name} ...", file=sys.stderr, flush=True)
             w2 = build_config(CFG_IDX, fmt, n_sink=S, n_recent=R, int8_query=q8)
-            w2.step_append()
-            _, p2 = time_steps(w2, max(10, args.steps // 2), 3, append=False)
+            ms2, att2, ph2, _ = time_steps(w2, args.steps, 3, settle_s=0.5)
             b2 = algorithmic_bytes(w2, fmt)
-            d2 = float(np.mean(p2["decode"]))
-            a2 = float(np.mean(p2["attend"]))
-            var[name] = {"decode_us": d2 * 1e3, "attend_us": a2 * 1e3,
-                         "decode_hbm_frac": b2 / (d2 * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            a2 = float(np.mean(att2))
+            var[name] = {"step_us": ms2 * 1e3, "attend_us": a2 * 1e3,
+                         "step_hbm_frac": b2 / (ms2 * 1e-3) / 1e9 / HBM_PEAK_GBS,
                          "attend_hbm_frac": attend_bytes(w2, fmt) / (a2 * 1e-3) / 1e9 / HBM_PEAK_GBS}
             del w2
             torch.cuda.empty_cache()
+        var["kv4_rl"] = {"step_us": ms * 1e3, "attend_us": att_ms * 1e3,
+                         "step_hbm_frac": result["config"]["step_hbm_frac"],
+                         "attend_hbm_frac": achieved / HBM_PEAK_GBS}
+        for v in var.values():
+            v["step_speedup_vs_bf16"] = var["bf16"]["step_us"] / v["step_us"]
         result["variants"] = var
     if args.mq > 0:
-        result["multi_query"] = time_multi_query(wl, args.mq, max(10, args.steps // 2), 3, abytes, us["decode"])
+        result["multi_query"] = time_multi_query(wl, args.mq, max(10, args.steps // 2), 3, abytes, us["step"])
     if not args.no_cpu:
         print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(wl)
+        one = cpu_baseline(wl, budget_s=8.0, threads=1)
+        result["cpu_baseline"]["single_core"] = {"value": one["value"], "cores": 1, "sample": one["sample"]}
     print(json.dumps(result), flush=True)
 
 

@@ -51,6 +51,31 @@ class GpuWorkload:
     def decode(self, stream=None):
         kv4.decode(self.cache, self.batch, self.q, self.out, self.lse, self.workspace, 1.0, stream)
 
+    def step_launches(self, stream=None):
+        """The benchmark's decode step as its three launches, in stream order:
+        the append of the step tokens with the plan in the same launch
+        (kv4_append_decode_phases with PHASE_PLAN), then ATTEND, then MERGE.
+        bench.py times exactly these calls; the parity tests run them too."""
+        def plan():
+            kv4.append_decode_phases(self.cache, self.step_batch, self.step_k, self.step_v, self.step_cu,
+                                     self.q, self.out, self.lse, self.workspace, kv4.PHASE_PLAN, stream=stream)
+
+        def attend():
+            kv4.decode_phases(self.cache, self.batch, self.q, self.out, self.lse, self.workspace,
+                              kv4.PHASE_ATTEND, stream=stream)
+
+        def merge():
+            kv4.decode_phases(self.cache, self.batch, self.q, self.out, self.lse, self.workspace,
+                              kv4.PHASE_MERGE, stream=stream)
+
+        return plan, attend, merge
+
+    def plan_chunk_pages(self) -> int:
+        """Middle pages per work item that the last plan chose (workspace header)."""
+        import torch
+
+        return int(self.workspace[:16].view(torch.int32).cpu()[2])
+
     # ------------------------------------------------------- host rebuild --
     def host_tokens(self, b: int):
         """bf16 bits K, V [L_b][Hkv][D] of sequence b, in position order."""

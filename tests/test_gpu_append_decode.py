@@ -132,3 +132,28 @@ def test_fused_multi_token_reappend(kv4, fmt):
         assert torch.equal(wl.cache.side, side)
     assert torch.equal(out.view(torch.int16), ref_out.view(torch.int16))
     assert torch.equal(lse.view(torch.int32), ref_lse.view(torch.int32))
+
+
+@pytest.mark.parametrize("fmt,q8", [(0, False), (0, True), (1, False), (2, False)],
+                         ids=["kv4", "kv4-int8q", "kv8", "bf16"])
+def test_fused_step_against_oracle(kv4, fmt, q8):
+    """The fused call itself against the oracle (not only against the other
+    HIP calls): config 1, every sequence appends its step token and the plan
+    shares the append's launch; then the page and side bytes of every
+    sequence, including the appended tokens, and every output."""
+    import torch
+
+    import parity_util as pu
+    from harness import build_config
+
+    wl = build_config(1, fmt, int8_query=q8, keep_inputs=True)
+    print(f"\nfused step vs oracle fmt={fmt} q8={q8} batch={wl.lengths.size}", flush=True)
+    ws = torch.empty_like(wl.workspace)
+    ws.fill_(0x3C)
+    kv4.append_decode_phases(wl.cache, wl.batch, wl.step_k, wl.step_v, wl.step_cu, wl.q, wl.out, wl.lse, ws, ALL)
+    torch.cuda.synchronize()
+    sample = np.arange(wl.lengths.size)
+    ocache, pt, lens = pu.compare_bytes(wl, sample)
+    m = pu.decode_metrics(wl, sample, ocache, pt, lens)
+    print(f"  rel_l2={m['rel_l2']:.3e} max_abs={m['max_abs']:.3e} lse={m['lse_abs']:.3e}", flush=True)
+    pu.assert_within(m)

@@ -163,3 +163,69 @@ def test_multiquery_rejects_bad_counts(kv4):
                         device="cuda")
     with pytest.raises(kv4.Kv4Error):
         kv4.decode_mq(wl.cache, wl.batch, q8, T, torch.zeros_like(q8), None, small)
+
+
+def test_multiquery_t64_qwen_shapes(kv4):
+    """The largest query count (KV4_MAX_QUERIES = 64) at Hq 32 / Hkv 8 / D 128:
+    16 blocks of four queries per sequence in the multi-column kernel, split
+    sequences, and sequences shorter than T."""
+    from harness import build_from_host
+
+    assert kv4.MAX_QUERIES == 64
+    lengths = np.array([2100, 300, 64, 40, 700, 145, 1], dtype=np.int32)
+    wl = build_from_host(1, 0, lengths=lengths)
+    _check(kv4, wl, 64, "qwen shapes T=64")
+
+
+@pytest.mark.parametrize("fmt", [0, 1], ids=["kv4", "kv8"])
+def test_chunked_prefill_256_in_4x64(kv4, fmt):
+    """A 256-token prompt built as four chunks of 64 tokens: after each chunk
+    is appended, one multi-query call attends its 64 positions causally over
+    the cache as it stands (query t of the chunk sees everything before it
+    and itself).  Qwen shapes with 16 sinks + 128 recent, so the middle INT4
+    region first appears in the third chunk.  Each chunk's cache bytes and
+    outputs are checked against the oracle given the same chunks.  kv4 runs
+    the multi-column kernel; kv8 runs one single-query unit per query."""
+    import torch
+
+    from harness.device import _bf16, _i32
+    from workloads import host_sequence
+
+    cfg = get_config(1)
+    B, P, T = 6, 256, 64
+    S, R = (cfg.n_sink, cfg.n_recent) if fmt == 0 else (0, 0)
+    lay = kv4.make_layout(cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim, S, R)
+    olay = oracle.make_layout(cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim, S, R)
+    npg = P // 16
+    # pages of sequence b are b*npg .. b*npg + npg - 1 in both caches, so the
+    # pools can be compared byte for byte
+    pt = np.arange(B * npg, dtype=np.int32).reshape(B, npg)
+    cache = kv4.alloc_cache(fmt, lay, B * npg, B)
+    ocache = oracle.HostCache(fmt, olay, B * npg, B)
+    toks = [host_sequence(cfg, 0, b, P)[:2] for b in range(B)]
+    ws = torch.empty(kv4.workspace_bytes(lay, B * T, npg), dtype=torch.uint8, device="cuda")
+    cu = np.arange(B + 1, dtype=np.int32) * T
+    for c in range(P // T):
+        n = (c + 1) * T
+        lens = np.full(B, n, dtype=np.int32)
+        k = np.concatenate([toks[b][0][c * T:n] for b in range(B)])
+        v = np.concatenate([toks[b][1][c * T:n] for b in range(B)])
+        batch = kv4.Batch(_i32(pt, "cuda"), _i32(lens, "cuda"))
+        kv4.append(cache, batch, _bf16(k, "cuda"), _bf16(v, "cuda"), _i32(cu, "cuda"))
+        oracle.append(ocache, pt, lens, None, k, v, cu)
+        qh = host_queries(cfg, 10 + c, B, T)
+        q = torch.from_numpy(qh.view(np.int16)).to("cuda").view(torch.bfloat16)
+        out = torch.zeros((B, T, cfg.num_q_heads, cfg.head_dim), dtype=torch.bfloat16, device="cuda")
+        lse = torch.zeros((B, T, cfg.num_q_heads), dtype=torch.float32, device="cuda")
+        kv4.decode_mq(cache, batch, q, T, out, lse, ws)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(cache.pages.cpu().numpy(), ocache.pages, err_msg=f"chunk {c}: pages")
+        if cache.side is not None:
+            np.testing.assert_array_equal(cache.side.cpu().numpy(), ocache.side[:cache.side.numel()],
+                                          err_msg=f"chunk {c}: side cache")
+        out64, lse64, gap = oracle.decode_mq(ocache, pt, lens, None, qh, T)
+        og = pu.bf16_bits_to_f64(out.view(torch.int16).cpu().numpy())
+        m = pu.metrics_from(og, lse.cpu().numpy().astype(np.float64), out64, lse64, gap)
+        print(f"\nprefill fmt={fmt} chunk {c} (positions {c * T}..{n - 1}): rel_l2={m['rel_l2']:.3e} "
+              f"max_abs={m['max_abs']:.3e} lse={m['lse_abs']:.3e}", flush=True)
+        pu.assert_within(m)

@@ -165,19 +165,73 @@ def test_config1_sampled(kv4):
     _check_all(wl, sample)
 
 
+def _bench_step(wl):
+    """One decode step exactly as bench.py times it: the fused append + plan
+    launch, then ATTEND, then MERGE (GpuWorkload.step_launches)."""
+    import torch
+
+    for launch in wl.step_launches():
+        launch()
+    torch.cuda.synchronize()
+
+
+def _config2_sample(wl, seed):
+    order = np.argsort(wl.lengths)
+    rng = np.random.default_rng(seed)
+    return np.unique(np.concatenate([order[:6], order[-6:], rng.choice(wl.lengths.size, 20, replace=False),
+                                     np.arange(8)]))   # a whole prompt group
+
+
 def test_config2_full_size_bench_launch(kv4):
-    """Config 2 at full size, in the benchmark's launch sequence (step append
-    of one token per sequence, then decode), checked on sampled sequences."""
+    """Config 2 at full size through the benchmark's own launch sequence
+    (kv4_append_decode_phases with the plan, then ATTEND and MERGE),
+    checked on sampled sequences: their page and side bytes, including the
+    step token the fused launch appended, and their outputs."""
     from harness import build_config
 
     wl = build_config(2, kv4.FMT_KV4, keep_inputs=True)
-    wl.step_append()
-    _run(kv4, wl)
-    order = np.argsort(wl.lengths)
-    rng = np.random.default_rng(0)
-    sample = np.unique(np.concatenate([order[:6], order[-6:], rng.choice(1024, 20, replace=False),
-                                       np.arange(8)]))   # a whole prompt group
-    _check_all(wl, sample)
+    _bench_step(wl)
+    chunk = wl.plan_chunk_pages()
+    print(f"\nconfig 2 plan: {chunk}-page chunks", flush=True)
+    assert chunk > 64, "the bench workload runs the two-page-ids-per-lane path"
+    _check_all(wl, _config2_sample(wl, 0))
+
+
+@pytest.mark.parametrize("fmt,S,R", [(1, 0, 0), (2, 0, 0), (0, 0, 0)], ids=["kv8", "bf16", "int4_plain"])
+def test_config2_full_size_variants(kv4, fmt, S, R):
+    """The reference variants of the precision ablation at the config-2 batch
+    (1,024 sequences, chunks of about 97 pages), through the benchmark's launch
+    sequence, against the oracle on sampled sequences."""
+    from harness import build_config
+
+    wl = build_config(2, fmt, keep_inputs=True, n_sink=S, n_recent=R)
+    _bench_step(wl)
+    chunk = wl.plan_chunk_pages()
+    print(f"\nconfig 2 fmt={fmt} S={S} R={R}: {chunk}-page chunks", flush=True)
+    assert chunk > 64
+    _check_all(wl, _config2_sample(wl, 1 + fmt))
+
+
+@pytest.mark.parametrize("fmt", [0, 1, 2], ids=["kv4", "kv8", "bf16"])
+def test_head_dim64_long_chunks(kv4, fmt):
+    """Head_dim 64 at the config-2 batch: enough pages that the plan cuts
+    chunks of more than 64 pages (two page ids per lane) for every format."""
+    import dataclasses
+
+    import workloads.configs as wc
+    from harness import build_config
+
+    cfg = dataclasses.replace(wc.CONFIGS[2], idx=93, name="config2-d64", head_dim=64)
+    wc.CONFIGS[93] = cfg
+    try:
+        wl = build_config(93, fmt, keep_inputs=True)
+        _bench_step(wl)
+        chunk = wl.plan_chunk_pages()
+        print(f"\nhead_dim 64 fmt={fmt}: {chunk}-page chunks", flush=True)
+        assert chunk > 64
+        _check_all(wl, _config2_sample(wl, 7))
+    finally:
+        del wc.CONFIGS[93]
 
 
 @pytest.mark.parametrize("int8_query", [False, True], ids=["bf16q", "int8q"])

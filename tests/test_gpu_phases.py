@@ -50,9 +50,10 @@ def test_plan_reused_across_layers(kv4, fmt):
 
 @pytest.mark.parametrize("fmt", [0, 1], ids=["kv4", "kv8"])
 def test_attend_repeated_on_one_plan(kv4, fmt):
-    """The attention phase hands units out from counters in the workspace and
-    resets them when it ends: many ATTEND + MERGE pairs on one PLAN, with
-    different queries in between, each give the bits of a full decode."""
+    """A plan is read, never consumed, by the attention phase (its unit
+    counter lives in LDS and starts at zero in every launch): many ATTEND +
+    MERGE pairs on one PLAN, with different queries in between, each give the
+    bits of a full decode."""
     import torch
 
     from harness import build_config
