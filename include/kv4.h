@@ -120,7 +120,9 @@ typedef struct {
 
 /* ---- versioning and status ------------------------------------------------ */
 int32_t kv4_abi_version(void);
-const char* kv4_status_string(kv4_status status); /* static string, never NULL */
+/* Text of a status code; any other integer gives "unknown status".  Static
+ * string, never NULL. */
+const char* kv4_status_string(int32_t status);
 
 /* ---- sizes (host) ---------------------------------------------------------- */
 /* INT4 page block per (page, kv head), 18 * head_dim bytes (D = head_dim,

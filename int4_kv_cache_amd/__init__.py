@@ -15,7 +15,8 @@ from dataclasses import dataclass
 from typing import Optional
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libkv4.so")
+# KV4_LIB loads another build of the same sources (the host-sanitizer test's)
+LIB_PATH = os.environ.get("KV4_LIB") or os.path.join(_HERE, "libkv4.so")
 
 FMT_KV4, FMT_KV8, FMT_BF16 = 0, 1, 2
 _PREFIX = {FMT_KV4: "kv4", FMT_KV8: "kv8", FMT_BF16: "kvbf16"}

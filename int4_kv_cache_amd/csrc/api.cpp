@@ -202,7 +202,9 @@ extern "C" {
 
 int32_t kv4_abi_version(void) { return KV4_ABI_VERSION; }
 
-const char* kv4_status_string(kv4_status s) {
+const char* kv4_status_string(int32_t s) {
+  // an int, not the enum: callers may pass any code, and a C++ enum object
+  // holding a value outside its enumerators' range is undefined
   switch (s) {
     case KV4_OK: return "ok";
     case KV4_ERR_INVALID_ARG: return "invalid argument";

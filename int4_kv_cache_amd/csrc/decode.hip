@@ -40,32 +40,14 @@ typedef __bf16 bf16x8_t __attribute__((__vector_size__(16)));
 typedef float f32x4_t __attribute__((__vector_size__(16)));
 typedef uint32_t u32x4_t __attribute__((__vector_size__(16)));
 
-#ifndef KV4_CHUNK_PAGES
-#define KV4_CHUNK_PAGES 32
-#endif
-#ifndef KV4_WAVES_PER_EU
-#define KV4_WAVES_PER_EU 2
-#endif
-#ifndef KV4_STAGES
-#define KV4_STAGES 2  // pipeline depth of the INT4 page loop (side tiles: KV4_STAGES8)
-#endif
-#ifndef KV4_MC_STAGES
-#define KV4_MC_STAGES 1  // pipeline depth of the multi-column kernel (2 measured 1.3% slower)
-#endif
-#ifndef KV4_UNITS_PER_WAVE
-#define KV4_UNITS_PER_WAVE 6  // work-list granularity: chunk size from the total work
-#endif
-#ifndef KV4_MERGE_K
-#define KV4_MERGE_K 4  // partial rows a merge task loads per round (8: 104 registers, 0.85 us slower)
-#endif
-#ifndef KV4_MAX_CHUNK
-#define KV4_MAX_CHUNK 128  // largest chunk of the single-query kernel (two page ids per lane)
-#endif
-#ifndef KV4_STAGES8
-#define KV4_STAGES8 2  // pipeline depth of the INT8 tile loops
-#endif
-constexpr int kChunkPages = KV4_CHUNK_PAGES;  // middle pages per work item (<= 64)
-static_assert(kChunkPages >= 1 && kChunkPages <= 64, "one lane holds one page id");
+// Tuning constants (each value measured against its neighbours on MI355X).
+constexpr int kChunkPages = 32;        // smallest chunk of middle pages per work item
+constexpr int kWavesPerEU = 2;         // attention waves per SIMD (215 of 256 registers)
+constexpr int kStages4 = 2;            // register pipeline depth of the INT4 page loop (3 and 4: 1% slower)
+constexpr int kStages8 = 2;            // pipeline depth of the INT8 tile loops; bf16 tiles use 1
+constexpr int kUnitsPerWave = 6;       // work-list granularity: chunk size from the total work
+constexpr int kMergeK = 4;             // partial rows a merge task loads per round (8: 104 registers, slower)
+constexpr int kMaxChunkPages = 128;    // largest chunk of the single-query kernel (two page ids per lane)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescale = 8.0f;  // re-reference the running max when it grows by 2^8
@@ -122,22 +104,17 @@ __device__ inline float max3(float a, float b, float c) {
 }
 __device__ inline float sbyte(uint32_t w, int k) { return float(int32_t(w << (24 - 8 * k)) >> 24); }
 
-// INT4 encoding: code c -> bf16 1 + (c + 8)/kEnc, nibble at mantissa bit kEncShift.
-#ifndef KV4_ENC_SHIFT
-#define KV4_ENC_SHIFT 0
-#endif
-constexpr int kEncShift = KV4_ENC_SHIFT;
-constexpr float kEnc = float(1 << (7 - kEncShift));          // 128
+// INT4 encoding: code c -> bf16 1 + (c + 8)/128, the nibble (sign bit flipped)
+// in the low four mantissa bits.
+constexpr float kEnc = 128.0f;
 constexpr float kEncConst = 1.0f + 8.0f / kEnc;              // 1.0625
-constexpr uint32_t kEncMask = 0x000F000Fu << kEncShift;
-constexpr uint32_t kEncBits = (0x3F80u | (8u << kEncShift)) * 0x00010001u;  // 1.0 with the sign bit of the code flipped
+constexpr uint32_t kEncMask = 0x000F000Fu;
+constexpr uint32_t kEncBits = 0x3F883F88u;                   // 1.0 with the sign bit of the code flipped
 
-// INT4: nibbles k and k+4 of d -> bf16 pair 1 + (code+8)/kEnc.
+// INT4: nibbles k and k+4 of d -> bf16 pair 1 + (code+8)/128.
 template <int K>
 __device__ inline uint32_t nib_pair(uint32_t d) {
-  constexpr int sh = 4 * K - kEncShift;
-  const uint32_t x = sh == 0 ? d : (sh < 0 ? (d << -sh) : (d >> sh));
-  return (x & kEncMask) ^ kEncBits;
+  return ((d >> (4 * K)) & kEncMask) ^ kEncBits;
 }
 __device__ inline uint32_t nib_pair_at(uint32_t d, int k) {  // k in 0..3 (unrolled)
   switch (k) {
@@ -148,11 +125,6 @@ __device__ inline uint32_t nib_pair_at(uint32_t d, int k) {  // k in 0..3 (unrol
   }
 }
 
-#ifndef KV4_SHIFT64
-#define KV4_SHIFT64 1
-#endif
-#if KV4_SHIFT64
-static_assert(kEncShift == 0, "the paired conversion assumes the code nibble at the bottom of the bf16");
 // x >> S for a register pair in one instruction (the compiler splits a
 // 64-bit shift into two 32-bit ones).
 template <int S>
@@ -175,7 +147,6 @@ __device__ inline void nib_pairs2(uint32_t a, uint32_t b, uint32_t& oa, uint32_t
     ob = (uint32_t(y >> 32) & kEncMask) ^ kEncBits;
   }
 }
-#endif
 
 // Cross-lane moves inside groups of 4 lanes (DPP quad permutations).
 __device__ inline float quad_xor1(float v) {
@@ -237,10 +208,6 @@ struct LaneOff {
 // bf16 tiles keep the default policy: the first are read again by the other
 // sequences of the group, the others are read in half-line pieces, and both
 // need their lines to stay in the caches in between.
-#ifndef KV4_NT_LOADS
-#define KV4_NT_LOADS 1  // 0: no hint anywhere
-#endif
-
 struct TileSrc {
   __amdgpu_buffer_rsrc_t r;
   __device__ inline TileSrc(const uint8_t* base, int bytes)
@@ -384,7 +351,6 @@ __device__ inline void qk_tile(const Unit<D>& u, const Tile<KIND, D>& T, float (
   } else if constexpr (KIND == kInt4Page) {
     const float c = -kEncConst * u.qsum;
     acc = f32x4_t{c, c, c, c};
-#if KV4_SHIFT64
 #pragma unroll
     for (int t = 0; t < NG; t += 2) {
       uint32_t a[4], b[4];
@@ -395,13 +361,6 @@ __device__ inline void qk_tile(const Unit<D>& u, const Tile<KIND, D>& T, float (
       acc = mfma(bf8(a[0], a[1], a[2], a[3]), u.bq[t], acc);
       acc = mfma(bf8(b[0], b[1], b[2], b[3]), u.bq[t + 1], acc);
     }
-#else
-#pragma unroll
-    for (int t = 0; t < NG; ++t) {
-      const uint32_t d = T.k[t];
-      acc = mfma(bf8(nib_pair<0>(d), nib_pair<1>(d), nib_pair<2>(d), nib_pair<3>(d)), u.bq[t], acc);
-    }
-#endif
   } else if constexpr (KIND == kInt8Tile) {
     acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -620,12 +579,11 @@ __device__ inline void pv_step(Unit<D>& u, const Tile<KIND, D>& T0, const Tile<K
   if constexpr (KIND == kInt4Page) {
     // -(1 + 8/kEnc) * sum over the positions of this row's A: the constant
     // part of the V codes' encoding, added to the output at the end.
-    constexpr uint32_t kNeg = (0xBF80u | (8u << kEncShift)) * 0x00010001u;
+    constexpr uint32_t kNeg = 0xBF88BF88u;  // -(1 + 8/128) in both halves
     const bf16x8_t ones = bf8(kNeg, kNeg, kNeg, kNeg);
     u.corr = mfma(a_hi, ones, u.corr);
     u.corr = mfma(a_lo, ones, u.corr);
   }
-#if KV4_SHIFT64
   if constexpr (KIND == kInt4Page) {
     // N-tiles j and j + 4 (head_dim 128) from one shift of each word pair:
     // words (pair, w) and (pair, w + 1) are adjacent, holding tiles 4w + j.
@@ -680,7 +638,6 @@ __device__ inline void pv_step(Unit<D>& u, const Tile<KIND, D>& T0, const Tile<K
     }
     return;
   }
-#endif
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     const bf16x8_t bv = v_operand<KIND, D>(T0, T1, t);
@@ -692,8 +649,8 @@ __device__ inline void pv_step(Unit<D>& u, const Tile<KIND, D>& T0, const Tile<K
 }
 
 // Runs n tiles (ptr(i), mask(i)) two at a time (a step).  STAGES = 1: load
-// then compute; 2: the next step's loads are in flight while a step is
-// computed; 3: the next two steps'.  Every load is issued unconditionally
+// then compute (bf16 tiles, whose registers leave no room for more); 2: the
+// next step's loads are in flight while a step is computed.  Every load is issued unconditionally
 // (past the end with an empty range) so the loop body has one fixed load
 // sequence and each wait covers exactly the step it needs.  Tile n (odd n)
 // reads as zeros and is masked.
@@ -724,7 +681,8 @@ __device__ inline void run_tiles(Unit<D>& u, int n, PtrFn ptr, MaskFn mask, int 
       setup();
       run(a0, a1, s);
     }
-  } else if constexpr (STAGES == 2) {
+  } else {
+    static_assert(STAGES == 2, "one or two pipeline stages");
     Tile<KIND, D> a0, a1, b0, b1;
     load(a0, a1, 0);
     setup();
@@ -735,22 +693,6 @@ __device__ inline void run_tiles(Unit<D>& u, int n, PtrFn ptr, MaskFn mask, int 
       load(a0, a1, s + 2);
       run(b0, b1, s + 1);
       if (s + 2 >= nsteps) break;
-    }
-  } else {
-    Tile<KIND, D> a0, a1, b0, b1, c0, c1;
-    load(a0, a1, 0);
-    load(b0, b1, 1);
-    setup();
-    for (int s = 0;; s += 3) {
-      load(c0, c1, s + 2);
-      run(a0, a1, s);
-      if (s + 1 >= nsteps) break;
-      load(a0, a1, s + 3);
-      run(b0, b1, s + 1);
-      if (s + 2 >= nsteps) break;
-      load(b0, b1, s + 4);
-      run(c0, c1, s + 2);
-      if (s + 3 >= nsteps) break;
     }
   }
 }
@@ -763,9 +705,8 @@ __device__ inline uint32_t range_mask(int lo, int hi) {  // bits [lo, hi) of 0..
 }
 
 // ---------------------------------------------------------------- worklist --
-constexpr int kMaxChunkPages = KV4_MAX_CHUNK;  // two page ids per lane in the single-query kernel
 constexpr int kMaxChunkPagesMc = 64;           // one page id per lane in the multi-column kernel
-static_assert(kMaxChunkPages == 64 || kMaxChunkPages == 128, "one or two page ids per lane");
+static_assert(kMaxChunkPages == 128, "the single-query kernel holds two page ids per lane");
 constexpr int kProtectedCost = 2;    // an INT8 tile costs about two INT4 pages
 
 struct SeqWork {
@@ -895,8 +836,8 @@ __device__ inline void plan_body(const DecodeParams& p, int units_per_item) {
   }
   unsigned long long total_pages = 0ull;
   (void)block_exclusive_scan(mine, part, total_pages);
-  // about KV4_UNITS_PER_WAVE units per resident wave
-  const unsigned long long denom = unsigned(KV4_UNITS_PER_WAVE) * unsigned(p.resident_waves > 0 ? p.resident_waves : 1);
+  // about kUnitsPerWave units per resident wave
+  const unsigned long long denom = unsigned(kUnitsPerWave) * unsigned(p.resident_waves > 0 ? p.resident_waves : 1);
   unsigned long long cl = (total_pages * unsigned(units_per_item) + denom - 1) / denom;
   const unsigned cmax = p.tq > 1 ? unsigned(kMaxChunkPagesMc) : unsigned(kMaxChunkPages);
   cl = cl < unsigned(kChunkPages) ? unsigned(kChunkPages) : (cl > cmax ? cmax : cl);
@@ -1049,7 +990,7 @@ __device__ inline uint32_t pool_unit(uint32_t t, uint32_t upi, uint32_t nitems, 
 }
 
 template <int FMT, int D>
-__global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(KV4_WAVES_PER_EU, 8))) void attention_kernel(
+__global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerEU, 8))) void attention_kernel(
     DecodeParams p) {
   constexpr int NG = D / 32, HB = 16 / NG, NT = D / 16;
   constexpr bool KV4 = FMT == kFmtKV4 || FMT == kFmtKV4Q8;
@@ -1097,7 +1038,7 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(KV
       const int col = c < p.max_pages ? c : p.max_pages - 1;
       r.x[k] = p.page_table[int64_t(d.b / p.nq) * p.max_pages + col];  // tq = 1: u = b * nq + t
       r.xp[k] = r.xn[k] = -1;
-      if constexpr (KV4 && KV4_NT_LOADS) {
+      if constexpr (KV4) {
         r.xp[k] = p.page_table[int64_t(bp / p.nq) * p.max_pages + col];
         r.xn[k] = p.page_table[int64_t(bn / p.nq) * p.max_pages + col];
       }
@@ -1113,7 +1054,7 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(KV
       pid[k] = ok ? r.x[k] : -1;
       const bool sh =
           ok && ((d.b > 0 && r.xp[k] == r.x[k]) || (d.b + 1 < p.batch * p.nq && r.xn[k] == r.x[k]));
-      shared[k] = __ballot(KV4 && KV4_NT_LOADS && sh);
+      shared[k] = __ballot(KV4 && sh);
     }
   };
   uint32_t t0 = grab();
@@ -1253,12 +1194,12 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(KV
         return range_mask(0 - r0, g.se - r0) | range_mask(S + rs - r0, S + r1 - r0) |
                range_mask(S - r0, S + r2 - r0);
       };
-      run_tiles<kInt8Tile, D, KV4_STAGES8, Q8, false>(u, ntiles, ptr, mask, lane, setup);
+      run_tiles<kInt8Tile, D, kStages8, Q8, false>(u, ntiles, ptr, mask, lane, setup);
     }
 
     // ---- middle pages of this item (at most kMaxChunkPages: NH page ids per lane)
     if (d.npg > 0) {
-      constexpr int ST = MAIN == kInt4Page ? KV4_STAGES : (MAIN == kInt8Tile ? KV4_STAGES8 : 1);
+      constexpr int ST = MAIN == kInt4Page ? kStages4 : (MAIN == kInt8Tile ? kStages8 : 1);
       // pages [0, ns) of the item are shared with a neighbouring sequence
       int ns = ~shared0[0] == 0ull ? kWave : int(__builtin_ctzll(~shared0[0]));
       if constexpr (NH == 2) {
@@ -1284,7 +1225,7 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(KV
         const uint64_t okm = (NH == 2 && i >= kWave) ? okmv[NH - 1] : okmv[0];
         return ((okm >> (i & (kWave - 1))) & 1ull) ? m : 0u;
       };
-      if constexpr (MAIN == kInt4Page && KV4_NT_LOADS) {
+      if constexpr (MAIN == kInt4Page) {
         run_tiles<MAIN, D, ST, Q8, false>(u, ns, ptr, mask, lane, setup);
         run_tiles<MAIN, D, ST, Q8, true>(
             u, d.npg - ns, [&](int i) { return ptr(ns + i); }, [&](int i) { return mask(ns + i); }, lane, setup);
@@ -1525,7 +1466,7 @@ __device__ inline void step_mc(McUnit& u, const McTile<KIND>& T0, const McTile<K
   u.l += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
 
   if constexpr (KIND == kInt4Page) {
-    constexpr uint32_t kNeg = (0xBF80u | (8u << kEncShift)) * 0x00010001u;
+    constexpr uint32_t kNeg = 0xBF88BF88u;  // -(1 + 8/128) in both halves
     const bf16x8_t ones = bf8(kNeg, kNeg, kNeg, kNeg);
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
@@ -1592,25 +1533,12 @@ __device__ inline void run_mc(McUnit& u, int n, PtrFn ptr, MaskFn mask, int lane
     const int i = 2 * s;
     step_mc<KIND>(u, t0, t1, mask(i), i + 1 < n ? mask(i + 1) : 0u, lane);
   };
-  if constexpr (KV4_MC_STAGES == 1) {
-    for (int s = 0; s < nsteps; ++s) {
-      McTile<KIND> a0, a1;
-      load(a0, a1, s);
-      setup();
-      run(a0, a1, s);
-    }
-  } else {
-    McTile<KIND> a0, a1, b0, b1;
-    load(a0, a1, 0);
+  // one stage: a second one measured 1.3% slower (registers)
+  for (int s = 0; s < nsteps; ++s) {
+    McTile<KIND> a0, a1;
+    load(a0, a1, s);
     setup();
-    for (int s = 0;; s += 2) {
-      load(b0, b1, s + 1);
-      run(a0, a1, s);
-      if (s + 1 >= nsteps) break;
-      load(a0, a1, s + 2);
-      run(b0, b1, s + 1);
-      if (s + 2 >= nsteps) break;
-    }
+    run(a0, a1, s);
   }
 }
 
@@ -1623,7 +1551,7 @@ __device__ inline uint32_t rows4(int r, int lo, int hi) {
   return hi > lo ? ((1u << hi) - 1u) & ~((1u << lo) - 1u) : 0u;
 }
 
-__global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(KV4_WAVES_PER_EU, 8))) void attention_mc_kernel(
+__global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerEU, 8))) void attention_mc_kernel(
     DecodeParams p) {
   constexpr int D = 128, NT = 8;
   const int lane = threadIdx.x & (kWave - 1);
@@ -1787,7 +1715,7 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeParams p) {
   // of a wave proceed independently.
   constexpr int QL = 16;      // lanes per task
   constexpr int E = D / QL;   // channels per lane
-  constexpr int K = KV4_MERGE_K;  // items per round
+  constexpr int K = kMergeK;  // items per round
   constexpr int RS = part_stride(D);
   const int sub = threadIdx.x & (QL - 1);
   const int Hq = p.num_q_heads;

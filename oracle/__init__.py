@@ -17,7 +17,8 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "kv4_oracle.c")
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# KV4_ORACLE_LIB loads another build of the same source (the sanitizer test's)
+_LIB_PATH = os.environ.get("KV4_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 
 FMT_KV4, FMT_KV8, FMT_BF16 = 0, 1, 2
 
