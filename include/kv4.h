@@ -21,9 +21,10 @@
  *     launch; faults inside a kernel surface at the caller's next stream sync.
  *   - The caller allocates and owns every buffer (pools, side cache, page
  *     table, lengths, q, out, lse, workspace).  The library allocates no
- *     device memory and keeps no mutable global state; calls on different
- *     streams are independent as long as they do not write the same pages,
- *     side blocks, outputs or workspace.
+ *     device memory and keeps no mutable global state, except the fixed
+ *     per-GPU scratch array of kv4_decode_attention_noalloc; calls on
+ *     different streams are independent as long as they do not write the same
+ *     pages, side blocks, outputs or workspace (or both use that scratch).
  *   - bf16 / fp16 values are passed as their raw 16-bit patterns (uint16_t).
  *   - Page pools and side caches must be zero-filled when first allocated.
  *     Decode reads whole pages and tiles; rows outside a sequence's context
@@ -57,7 +58,7 @@
 extern "C" {
 #endif
 
-#define KV4_ABI_VERSION 4
+#define KV4_ABI_VERSION 5
 
 typedef enum {
   KV4_OK = 0,
@@ -331,6 +332,28 @@ kv4_status kvbf16_decode_attention_mq(const kv4_layout* layout, const kv4_cache*
                                       int32_t num_queries, float softmax_scale,
                                       uint16_t* out, float* lse, void* workspace,
                                       size_t workspace_bytes, hipStream_t stream);
+
+/* ---- decode without a caller workspace ------------------------------------------
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * computation and arguments as kv4_decode_attention, without the workspace.
+ * The library keeps one scratch array of KV4_NOALLOC_SCRATCH_BYTES per GPU in
+ * its code object (each GPU the library runs on holds it until the process
+ * ends) and uses the current device's.  It allocates nothing, neither device
+ * nor host memory.  A batch whose kv4_decode_workspace_size exceeds
+ * KV4_NOALLOC_SCRATCH_BYTES is rejected with KV4_ERR_WORKSPACE before
+ * anything is launched (about 3,900 work items at 32 query heads and
+ * head_dim 128, e.g. 118 sequences with page tables of 1,040 columns).
+ * Every call on one GPU uses that GPU's one array: calls that overlap on a
+ * GPU (other streams, other host threads) race and must be ordered by the
+ * caller.  The array's contents are never read before a call writes them, so
+ * nothing needs clearing between calls.  KV4_ERR_LAUNCH also reports a failed
+ * lookup of the array's device address (once per device, on first use). */
+#define KV4_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+kv4_status kv4_decode_attention_noalloc(const kv4_layout* layout, const kv4_cache* cache,
+                                        const kv4_batch* batch, const uint16_t* q,
+                                        float softmax_scale, uint16_t* out, float* lse,
+                                        hipStream_t stream);
 
 /* ---- capacity model (host) ---------------------------------------------------
  * The pages credit part of the end-to-end gain to the higher concurrency a

@@ -62,6 +62,7 @@ EXPORTS = [
     "kv4_decode_phases", "kv8_decode_phases", "kvbf16_decode_phases",
     "kv4_decode_attention_mq", "kv8_decode_attention_mq", "kvbf16_decode_attention_mq",
     "kv4_append_decode_phases", "kv8_append_decode_phases", "kvbf16_append_decode_phases",
+    "kv4_decode_attention_noalloc",
     "kv4_cache_capacity",
     "kv4_probe_blocks", "kv4_hbm_read_probe",
 ]
@@ -102,6 +103,8 @@ def load(path: Optional[str] = None):
         f = getattr(L, f"{pre}_append_decode_phases")
         f.restype = ctypes.c_int
         f.argtypes = [P, P, P, P, P, P, i32, P, ctypes.c_float, P, P, P, sz, ctypes.c_uint32, P]
+    L.kv4_decode_attention_noalloc.restype = ctypes.c_int
+    L.kv4_decode_attention_noalloc.argtypes = [P, P, P, P, ctypes.c_float, P, P, P]
     L.kv4_decode_workspace_size.restype = ctypes.c_int
     L.kv4_decode_workspace_size.argtypes = [P, i32, i32, ctypes.POINTER(sz)]
     L.kv4_cache_capacity.restype = ctypes.c_int
@@ -217,6 +220,20 @@ def decode(cache: Cache, batch: Batch, q, out, lse, workspace, softmax_scale: fl
                              float(softmax_scale), _ptr(out), _ptr(lse), _ptr(workspace),
                              int(workspace.numel()), _stream(stream))
     _check(fn, st)
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def decode_noalloc(cache: Cache, batch: Batch, q, out, lse, softmax_scale: float = 1.0, stream=None):
+    """kv4_decode_attention without a workspace: the library's fixed per-GPU
+    scratch (NOALLOC_SCRATCH_BYTES) holds the plan and partials.  kv4 only."""
+    if cache.fmt != FMT_KV4:
+        raise ValueError("decode_noalloc exists for the kv4 format only")
+    lay, cd, bd = cache.layout, cache.desc(), batch.desc()
+    st = load().kv4_decode_attention_noalloc(ctypes.byref(lay), ctypes.byref(cd), ctypes.byref(bd), _ptr(q),
+                                             float(softmax_scale), _ptr(out), _ptr(lse), _stream(stream))
+    _check("kv4_decode_attention_noalloc", st)
 
 
 MAX_QUERIES = 64

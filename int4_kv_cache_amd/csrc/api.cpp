@@ -104,9 +104,11 @@ kv4_status append_impl(int fmt, const kv4_layout* L, const kv4_cache* c, const k
 
 // Checks the decode arguments and fills `p` and the kernel format `kfmt`.
 // With an empty batch it returns KV4_OK and sets p.batch = 0 (nothing to launch).
+// check_only: every check, including the workspace size against ws_bytes, but
+// no workspace address yet (ws may be null; p.ws is left empty).
 kv4_status decode_params(int fmt, const kv4_layout* L, const kv4_cache* c, const kv4_batch* b,
                          const uint16_t* q, float sm, uint16_t* out, float* lse, void* ws, size_t ws_bytes,
-                         unsigned phases, int32_t nq, kv4::DecodeParams& p, int& kfmt) {
+                         unsigned phases, int32_t nq, kv4::DecodeParams& p, int& kfmt, bool check_only = false) {
   if (phases < 1u || phases > 7u) return KV4_ERR_INVALID_ARG;
   if (nq < 1 || nq > KV4_MAX_QUERIES) return KV4_ERR_INVALID_ARG;
   kv4_status s = layout_check(L, fmt);
@@ -122,7 +124,7 @@ kv4_status decode_params(int fmt, const kv4_layout* L, const kv4_cache* c, const
   }
   p = kv4::DecodeParams{};
   if (b->batch == 0) return KV4_OK;
-  if (!ws) return KV4_ERR_INVALID_ARG;
+  if (!ws && !check_only) return KV4_ERR_INVALID_ARG;
   if ((phases & (KV4_PHASE_ATTEND | KV4_PHASE_MERGE)) && !out) return KV4_ERR_INVALID_ARG;
   if ((phases & KV4_PHASE_ATTEND) && !q) return KV4_ERR_INVALID_ARG;
   if (!(sm > 0.0f) || sm > 3.0e38f) return KV4_ERR_INVALID_ARG;  // positive and finite
@@ -156,7 +158,7 @@ kv4_status decode_params(int fmt, const kv4_layout* L, const kv4_cache* c, const
   p.n_recent = fmt == kFmtKV4 ? L->n_recent : 0;
   p.block_bytes = int64_t(block_bytes(L, fmt));
   p.side_bytes = int64_t(side_bytes(L));
-  p.ws = kv4::carve_workspace(ws, nv, b->max_pages, L->num_q_heads, L->head_dim);
+  if (!check_only) p.ws = kv4::carve_workspace(ws, nv, b->max_pages, L->num_q_heads, L->head_dim);
   if (!protected_set(L, fmt)) {
     p.side = nullptr;
     p.num_slots = 0;
@@ -305,6 +307,21 @@ kv4_status kvbf16_decode_attention_mq(const kv4_layout* L, const kv4_cache* c, c
                                       const uint16_t* q, int32_t num_queries, float sm, uint16_t* out,
                                       float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
   return decode_impl(kFmtBF16, L, c, b, q, sm, out, lse, ws, ws_bytes, kAllPhases, stream, num_queries);
+}
+
+kv4_status kv4_decode_attention_noalloc(const kv4_layout* L, const kv4_cache* c, const kv4_batch* b,
+                                        const uint16_t* q, float sm, uint16_t* out, float* lse,
+                                        hipStream_t stream) {
+  // every argument check, and the batch's workspace size against the fixed
+  // scratch, happens on the host before the scratch address is looked up
+  kv4::DecodeParams p;
+  int kfmt = kFmtKV4;
+  const kv4_status s = decode_params(kFmtKV4, L, c, b, q, sm, out, lse, nullptr, KV4_NOALLOC_SCRATCH_BYTES,
+                                     kAllPhases, 1, p, kfmt, /*check_only=*/true);
+  if (s != KV4_OK || p.batch == 0) return s;
+  void* ws = nullptr;
+  if (kv4::noalloc_scratch(&ws) != hipSuccess) return KV4_ERR_LAUNCH;
+  return decode_impl(kFmtKV4, L, c, b, q, sm, out, lse, ws, KV4_NOALLOC_SCRATCH_BYTES, kAllPhases, stream);
 }
 
 kv4_status kv4_cache_capacity(const kv4_layout* L, int32_t format, int32_t num_layers, const int32_t* seq_lens,

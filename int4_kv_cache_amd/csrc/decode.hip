@@ -33,6 +33,8 @@
 #include "kv4_launch.h"
 #include "append_body.h"
 
+#include <mutex>
+
 namespace kv4 {
 namespace {
 
@@ -1900,6 +1902,35 @@ DecodeWorkspace carve_workspace(void* base, int32_t batch, int32_t max_pages, in
   w.partials = reinterpret_cast<float*>(q);
   w.max_items = max_items;
   return w;
+}
+
+// ---------------------------------------------- allocation-free decode --
+// Scratch of kv4_decode_attention_noalloc (the plan and the partials of one
+// decode call), for callers that cannot allocate device memory.  Every GPU
+// the library runs on holds its own copy until the process ends.  In host
+// code `scratch` names a host-side stand-in, not the device array: the
+// device address is taken once per device, with that device current, and
+// only that address is ever handed to a kernel.
+static __device__ __align__(256) uint8_t scratch[KV4_NOALLOC_SCRATCH_BYTES];
+
+hipError_t noalloc_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* a = nullptr;
+    e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (a == nullptr) return hipErrorInvalidSymbol;
+    addr[dev] = a;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_decode(int fmt, const DecodeParams& p, int head_dim, unsigned phases, hipStream_t stream,

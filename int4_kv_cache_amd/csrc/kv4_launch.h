@@ -80,6 +80,10 @@ DecodeWorkspace carve_workspace(void* base, int32_t batch, int32_t max_pages, in
 hipError_t launch_decode(int fmt, const DecodeParams& p, int head_dim, unsigned phases, hipStream_t stream,
                          const AppendParams* append = nullptr);
 
+// Device address of this device's KV4_NOALLOC_SCRATCH_BYTES scratch array
+// (looked up once per device; the current device's).
+hipError_t noalloc_scratch(void** ptr);
+
 hipError_t launch_probe(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream);
 int32_t probe_blocks();
 

@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.kv4_abi_version() == 4
+    assert lib.kv4_abi_version() == 5
     for code, text in kv4.STATUS.items():
         assert lib.kv4_status_string(code).decode() == text
     assert lib.kv4_status_string(12345).decode() == "unknown status"
@@ -165,3 +165,32 @@ def test_host_argument_errors_return_before_launch(lib):
     # probe
     assert lib.kv4_hbm_read_probe(fake, 17, fake, None) == -1
     assert lib.kv4_hbm_read_probe(None, 16, fake, None) == -1
+
+
+def test_noalloc_rejects_on_the_host(lib):
+    """kv4_decode_attention_noalloc checks arguments and the batch's workspace
+    size against its fixed scratch before it looks up or touches the device
+    (fake pointers, never dereferenced)."""
+    fake = 0x1000
+    lay = kv4.make_layout(32, 8, 128, 16, 128)
+    cache = kv4.CacheDesc(fake, 10, fake, 128)
+
+    def call(batch, q=fake, out=fake, layout=lay):
+        return lib.kv4_decode_attention_noalloc(ctypes.byref(layout), ctypes.byref(cache),
+                                                ctypes.byref(batch) if batch else None, q, 1.0, out, None, None)
+
+    # 128 sequences with page tables of 1,040 columns need about 72 MB of workspace
+    big = kv4.BatchDesc(fake, 1040, fake, None, 128)
+    assert kv4.workspace_bytes(lay, 128, 1040) > kv4.NOALLOC_SCRATCH_BYTES
+    assert call(big) == -3
+    # the size that still fits is the one kv4_decode_workspace_size reports
+    n_fit = max(b for b in range(1, 200) if kv4.workspace_bytes(lay, b, 1040) <= kv4.NOALLOC_SCRATCH_BYTES)
+    assert call(kv4.BatchDesc(fake, 1040, fake, None, n_fit + 1)) == -3
+    assert 100 <= n_fit < 128
+    assert call(None) == -1
+    assert call(kv4.BatchDesc(fake, 4, fake, None, 2), q=None) == -1
+    assert call(kv4.BatchDesc(fake, 4, fake, None, 2), out=None) == -1
+    assert call(kv4.BatchDesc(fake, 0, fake, None, 2)) == -1
+    assert call(kv4.BatchDesc(fake, 4, fake, None, 2), layout=kv4.make_layout(32, 8, 96, 0, 0)) == -2
+    # an empty batch is a no-op that needs no device
+    assert call(kv4.BatchDesc(None, 4, None, None, 0)) == 0
