@@ -235,7 +235,9 @@ kv4_status kvbf16_decode_attention(const kv4_layout* layout, const kv4_cache* ca
  * unchanged -- e.g. every layer of a decode step, whose layers share the page
  * table and seq_lens but have their own cache and q.  A plan is only valid
  * for the function (format) that made it.  ATTEND+MERGE pairs that share a
- * workspace must not overlap (the partials live there).  Arguments and
+ * workspace must not overlap: the partials live there, and so do the counters
+ * from which an ATTEND launch's waves draw the end of the work list (the
+ * launch leaves them as it found them).  Arguments and
  * errors as for *_decode_attention; `phases` outside 1..7 is
  * KV4_ERR_INVALID_ARG; q/out/cache are not read by PLAN alone (may be NULL). */
 #define KV4_PHASE_PLAN 1u

@@ -652,10 +652,13 @@ __device__ inline void pv_step(Unit<D>& u, const Tile<KIND, D>& T0, const Tile<K
 
 // Runs n tiles (ptr(i), mask(i)) two at a time (a step).  STAGES = 1: load
 // then compute (bf16 tiles, whose registers leave no room for more); 2: the
-// next step's loads are in flight while a step is computed.  Every load is issued unconditionally
-// (past the end with an empty range) so the loop body has one fixed load
-// sequence and each wait covers exactly the step it needs.  Tile n (odd n)
-// reads as zeros and is masked.
+// next step's loads are in flight while a step is computed.  Every load is
+// issued unconditionally (past the end with an empty range) so the loop body
+// has one fixed load sequence and each wait covers exactly the step it
+// needs.  Tile n (odd n) reads as zeros and is masked.  setup(0) is called
+// once the first step's loads are in flight, setup(1) after the first step
+// and setup(2) after the second (and again on later steps; the caller acts on
+// the first call of each).
 template <int KIND, int D, int STAGES, bool Q8, bool NT, class PtrFn, class MaskFn, class SetupFn>
 __device__ inline void run_tiles(Unit<D>& u, int n, PtrFn ptr, MaskFn mask, int lane, SetupFn setup) {
   if (n <= 0) return;
@@ -680,20 +683,23 @@ __device__ inline void run_tiles(Unit<D>& u, int n, PtrFn ptr, MaskFn mask, int 
     for (int s = 0; s < nsteps; ++s) {
       Tile<KIND, D> a0, a1;
       load(a0, a1, s);
-      setup();
+      setup(0);
       run(a0, a1, s);
+      setup(s + 1 < 2 ? s + 1 : 2);
     }
   } else {
     static_assert(STAGES == 2, "one or two pipeline stages");
     Tile<KIND, D> a0, a1, b0, b1;
     load(a0, a1, 0);
-    setup();
+    setup(0);
     for (int s = 0;; s += 2) {
       load(b0, b1, s + 1);
       run(a0, a1, s);
+      setup(1);
       if (s + 1 >= nsteps) break;
       load(a0, a1, s + 2);
       run(b0, b1, s + 1);
+      setup(2);
       if (s + 2 >= nsteps) break;
     }
   }
@@ -815,6 +821,8 @@ __device__ inline unsigned long long block_exclusive_scan(unsigned long long v, 
   return before + inc - v;
 }
 
+__device__ inline void pool_reset(const DecodeParams& p, int tid, int nthreads);
+
 // One workgroup: chooses the chunk size from the total work, numbers the
 // partial slots of split sequences and writes the item descriptors: all full
 // chunks first, then the remaining (shorter) items in decreasing cost (pages
@@ -827,6 +835,7 @@ __device__ inline void plan_body(const DecodeParams& p, int units_per_item) {
   __shared__ uint32_t nmerge;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
   const int nv = p.batch * n_blocks(p);  // work blocks
+  pool_reset(p, tid, 1024);
   for (int i = tid; i < kMaxChunkPages + 2; i += 1024) bucket[i] = 0u;
   if (tid == 0) nmerge = 0u;
   SeqWork w0{};
@@ -971,24 +980,91 @@ __device__ inline ItemDesc decode_item(const RawItem& r) {
   return d;
 }
 
-// Per-CU unit pool.  One workgroup per CU holds both waves of every SIMD.
-// Workgroup c owns one item of every C consecutive items of the list
-// (costliest first), in serpentine order -- c, 2C - 1 - c, 2C + c, ... -- so
-// the CUs get equal shares of every cost, and its waves take the units of
-// those items (upi per item, next to each other) in ticket order from a
-// counter in LDS.  The two waves of a SIMD do not progress at the same rate
-// (the older one wins issue), so a fixed split between them would leave one
-// wave per SIMD running alone at the end.
+// Work distribution.  One workgroup per CU holds both waves of every SIMD.
+// The list (full chunks first, then the other items in decreasing cost) is
+// cut in two.  The head -- about three quarters of the items, a whole number
+// of rounds of C items (C workgroups) -- is shared out: workgroup c owns one
+// item of every round, in serpentine order (c, 2C - 1 - c, 2C + c, ...), so
+// the shares hold equal amounts of every cost, and its waves take the units
+// of those items (upi per item, next to each other) in ticket order from a
+// counter in LDS, so a faster wave takes more of them.  The tail, the
+// cheapest items, is one queue for the whole GPU: a wave whose workgroup's
+// share is used up takes its next unit there, from a device counter.  CUs and
+// XCDs do not run at the same speed and the plan's cost estimate is not
+// exact; the tail absorbs both, and it ends on the smallest units.
+//
+// The device counters sit on 128-byte lines of the workspace: line 0 counts
+// the waves that have finished, line 1 is the tail's ticket counter.  The plan
+// zeroes them, and the last wave of an attention launch to finish zeroes them
+// again, so one plan serves any number of attention launches.
+constexpr int kCtrStride = 32;  // uint32 words per counter line
+constexpr int kSc1 = 16;        // buffer cache-policy bit of device-coherent stores
+
+// items in the shared-out head of a list of nitems items, for C workgroups
+__device__ inline uint32_t head_items(uint32_t nitems, uint32_t C) { return (nitems - nitems / 4u) / C * C; }
+
+// LDS ticket of the workgroup's share
 __device__ inline uint32_t pool_ticket(uint32_t* counter, int lane) {
   uint32_t t = 0u;
   if (lane == 0) t = atomicAdd(counter, 1u);
   return uint32_t(uniform(int(t)));
 }
-// the unit of ticket t, or `units` past the end of the workgroup's share
-__device__ inline uint32_t pool_unit(uint32_t t, uint32_t upi, uint32_t nitems, uint32_t units) {
+// the unit of ticket t of this workgroup's share, or `units` past its end
+__device__ inline uint32_t pool_unit(uint32_t t, uint32_t upi, uint32_t nhead, uint32_t units) {
   const uint32_t round = t / upi, C = gridDim.x;
   const uint32_t item = round * C + ((round & 1u) ? C - 1u - blockIdx.x : blockIdx.x);
-  return item < nitems ? item * upi + t % upi : units;
+  return item < nhead ? item * upi + t % upi : units;
+}
+
+// Atomic add of 1 by lane 0 of the wave when `enable` (wave-uniform),
+// returned in lane 0; otherwise no memory access.  The buffer range is the
+// 4-byte counter (or empty), and the other lanes' offsets lie past it:
+// buffer accesses outside the range are dropped (an atomic returns 0), so the
+// wave makes at most one increment with no branch around the atomic.  (A
+// global atomic under `if (lane == 0)` inside the unit loop makes the
+// compiler keep the page loads' buffer descriptors in vector registers, with
+// a readfirstlane loop around every page load.)
+__device__ inline uint32_t lane0_atomic_add(uint32_t* ctr, bool enable, int lane) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(ctr, short(0), enable ? 4 : 0, 0x00020000);
+  return uint32_t(__builtin_amdgcn_raw_ptr_buffer_atomic_add_i32(1, r, lane == 0 ? 0 : 64, 0, 0));
+}
+
+// A drawn unit: from the workgroup's share (`local` < units), or a pending
+// tail ticket (`raw`, lane 0) to be read once its atomic has returned.
+struct Ticket {
+  uint32_t local, raw;
+};
+__device__ inline Ticket pool_issue(const DecodeParams& p, uint32_t* counter, uint32_t upi, uint32_t nhead,
+                                    uint32_t units, int lane) {
+  const uint32_t u = pool_unit(pool_ticket(counter, lane), upi, nhead, units);
+  return Ticket{u, lane0_atomic_add(p.ws.ctr + kCtrStride, u >= units, lane)};
+}
+// The unit of a drawn ticket, or `units` when the list is used up.
+// Wave-uniform.
+__device__ inline uint32_t pool_finish(const Ticket& k, uint32_t upi, uint32_t nhead, uint32_t units) {
+  if (k.local < units) return k.local;
+  const uint32_t g = uint32_t(uniform(int(k.raw))), tail = units - nhead * upi;
+  return g < tail ? nhead * upi + g : units;
+}
+
+// A wave that has drawn its last ticket: after every memory operation it
+// issued has completed (so its ticket atomics have been made), it counts
+// itself finished; the last wave of the launch zeroes the device counters.
+__device__ inline void pool_leave(const DecodeParams& p, int lane) {
+  __builtin_amdgcn_s_waitcnt(0);
+  const uint32_t waves = gridDim.x * (blockDim.x / kWave);
+  const uint32_t n = uint32_t(uniform(int(lane0_atomic_add(p.ws.ctr, true, lane))));
+  if (n + 1u == waves) {
+    const __amdgpu_buffer_rsrc_t all =
+        __builtin_amdgcn_make_buffer_rsrc(p.ws.ctr, short(0), int(2 * kCtrStride * sizeof(uint32_t)), 0x00020000);
+    __builtin_amdgcn_raw_buffer_store_b32(0u, all, uint32_t(lane) * uint32_t(kCtrStride * sizeof(uint32_t)), 0, kSc1);
+  }
+}
+
+// Zeroes the device counters (the plan; nthreads threads of one workgroup).
+__device__ inline void pool_reset(const DecodeParams& p, int tid, int nthreads) {
+  for (int v = tid; v < 2; v += nthreads)
+    __hip_atomic_store(p.ws.ctr + v * kCtrStride, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int FMT, int D>
@@ -1010,13 +1086,19 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(kW
   const uint32_t units = nitems * uint32_t(UPI);
   if (units == 0) return;
 
-  // Units come from the per-CU pool.  The next units are known in advance:
-  // the descriptor of unit k+2 and the page ids of unit k+1 are loaded when
-  // unit k starts.
+  // Units come from the pool (see pool_issue).  A wave works on one unit
+  // and prepares the next one: its ticket is drawn when the unit starts, and
+  // resolved after the unit's first step (by then the atomic has returned),
+  // which also issues the next descriptor's load; after the second step the
+  // descriptor is decoded and the next unit's page ids are loaded.  So a wave
+  // holds one unit beyond the one it works on, and when the pool runs dry the
+  // waves finish within about one unit of each other.
+  const uint32_t nhead = head_items(nitems, gridDim.x);
   __shared__ uint32_t next_ticket;
   if (threadIdx.x == 0) next_ticket = 0u;
   __syncthreads();
-  auto grab = [&]() -> uint32_t { return pool_unit(pool_ticket(&next_ticket, lane), UPI, nitems, units); };
+  auto issue = [&]() -> Ticket { return pool_issue(p, &next_ticket, UPI, nhead, units, lane); };
+  auto finish = [&](const Ticket& k) -> uint32_t { return pool_finish(k, UPI, nhead, units); };
   auto item_of = [&](uint32_t t) -> uint32_t { return (t < units ? t : units - 1) / uint32_t(UPI); };
   // Page ids of an item, one per lane, loaded one unit ahead as raw page-table
   // words: this lane's page and the pages at the same index of the work
@@ -1059,10 +1141,8 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(kW
       shared[k] = __ballot(KV4 && sh);
     }
   };
-  uint32_t t0 = grab();
-  uint32_t t1 = grab();
+  uint32_t t0 = finish(issue());
   ItemDesc d0 = decode_item(load_item(p, item_of(t0)));
-  RawItem r1 = load_item(p, item_of(t1));
   Pids pid0 = fetch_pids(d0);
 
   while (t0 < units) {
@@ -1070,11 +1150,26 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(kW
     int pid0v[NH];
     uint64_t shared0[NH];
     resolve_pids(pid0, d0, pid0v, shared0);
-    // ---- run-ahead for the following units (fixed position, unconditional)
-    const uint32_t t2 = grab();
-    const RawItem r2 = load_item(p, item_of(t2));
-    const ItemDesc d1 = decode_item(r1);
-    const Pids pid1 = fetch_pids(d1);
+    // ---- the next unit: ticket now, the rest in `advance` (from setup(1)
+    // and setup(2), and after the unit for what a short unit left undone)
+    const Ticket k1 = issue();
+    uint32_t t1 = units;
+    RawItem r1;
+    ItemDesc d1;
+    Pids pid1;
+    int next_stage = 0;
+    auto advance = [&](int upto) {
+      if (next_stage < 1 && upto >= 1) {
+        next_stage = 1;
+        t1 = finish(k1);
+        r1 = load_item(p, item_of(t1));
+      }
+      if (next_stage < 2 && upto >= 2) {
+        next_stage = 2;
+        d1 = decode_item(r1);
+        pid1 = fetch_pids(d1);
+      }
+    };
 
     const int rem = int(t0 % uint32_t(UPI));
     const int h = rem / NHB, hb = rem % NHB;
@@ -1108,7 +1203,11 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(kW
       u.l = 0.f;
       u.qk_scale = p.softmax_scale * kLog2e;
     }
-    auto setup = [&]() {
+    auto setup = [&](int stage) {
+      if (stage > 0) {
+        advance(stage);
+        return;
+      }
       if (!pending) return;
       pending = false;
       if constexpr (Q8) {
@@ -1280,12 +1379,12 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(kW
       }
     }
     // ---- rotate the run-ahead state
+    advance(2);  // what a unit with fewer than two steps left undone
     t0 = t1;
-    t1 = t2;
     d0 = d1;
-    r1 = r2;
     pid0 = pid1;
   }
+  pool_leave(p, lane);
 }
 
 // ------------------------------------------------ multi-query attention --
@@ -1564,12 +1663,16 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(kW
   const uint32_t nitems = p.ws.header[1];
   const uint32_t units = nitems * uint32_t(H);
   if (units == 0) return;
-  // units (item, kv head) from the per-CU pool
+  // units (item, kv head) from the pool; the next unit's ticket is drawn
+  // when a unit starts
+  const uint32_t nhead = head_items(nitems, gridDim.x);
   __shared__ uint32_t next_ticket;
   if (threadIdx.x == 0) next_ticket = 0u;
   __syncthreads();
-  auto grab = [&]() -> uint32_t { return pool_unit(pool_ticket(&next_ticket, lane), uint32_t(H), nitems, units); };
-  for (uint32_t t0 = grab(); t0 < units; t0 = grab()) {
+  Ticket k = pool_issue(p, &next_ticket, uint32_t(H), nhead, units, lane);
+  for (uint32_t t0 = pool_finish(k, uint32_t(H), nhead, units); t0 < units;
+       t0 = pool_finish(k, uint32_t(H), nhead, units)) {
+    k = pool_issue(p, &next_ticket, uint32_t(H), nhead, units, lane);
     const ItemDesc d = decode_item(load_item(p, t0 / uint32_t(H)));
     const int h = int(t0 % uint32_t(H));
     const int bseq = d.b / nqb, tb = (d.b % nqb) * p.tq;  // sequence, first query of the block
@@ -1701,6 +1804,7 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(kW
       }
     }
   }
+  pool_leave(p, lane);
 }
 
 // ----------------------------------------------------------------- merge ---
@@ -1812,7 +1916,7 @@ hipError_t launch_fd(DecodeParams p, unsigned phases, const AppendParams* append
   const bool mc = FMT == kFmtKV4 && D == 128 && p.nq > 1 && G <= 16 && 16 % G == 0;
   p.tq = mc ? 16 / G : 1;
   // the work list is sized for the attention grid, so both use the same count
-  const int blocks = cus;  // one workgroup per CU (the per-CU unit pool)
+  const int blocks = cus;  // one workgroup per CU (the per-CU share of the list)
   p.resident_waves = blocks * (kAttnThreads / kWave);
   if (phases & 1u) {
     const int units_per_item = mc ? p.num_kv_heads : p.num_kv_heads * ((G + HB - 1) / HB);
@@ -1879,13 +1983,12 @@ size_t decode_workspace_bytes(int32_t batch, int32_t max_pages, int32_t num_q_he
   s += 3 * align256(sizeof(int32_t) * size_t(batch));  // item_base, item_count, merge_list
   s += align256(2 * sizeof(int4) * size_t(max_items)); // items
   s += align256(sizeof(float) * size_t(max_items) * num_q_heads * part_stride(head_dim));
+  s += 2 * kCtrStride * sizeof(uint32_t);  // work counters
   return s;
 }
 
 DecodeWorkspace carve_workspace(void* base, int32_t batch, int32_t max_pages, int32_t num_q_heads,
                                 int32_t head_dim) {
-  (void)num_q_heads;
-  (void)head_dim;
   const int64_t max_items = max_items_of(batch, max_pages);
   uint8_t* q = static_cast<uint8_t*>(base);
   DecodeWorkspace w;
@@ -1900,6 +2003,8 @@ DecodeWorkspace carve_workspace(void* base, int32_t batch, int32_t max_pages, in
   w.items = reinterpret_cast<int4*>(q);
   q += align256(2 * sizeof(int4) * size_t(max_items));
   w.partials = reinterpret_cast<float*>(q);
+  q += align256(sizeof(float) * size_t(max_items) * num_q_heads * part_stride(head_dim));
+  w.ctr = reinterpret_cast<uint32_t*>(q);
   w.max_items = max_items;
   return w;
 }

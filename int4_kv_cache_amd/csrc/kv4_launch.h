@@ -39,6 +39,7 @@ struct DecodeWorkspace {
   int32_t* merge_list;   // [batch] split sequences
   int4* items;           // [max_items][2] work-item descriptors (two int4 each)
   float* partials;       // [max_items][num_q_heads][head_dim + 4]: o, m, l, padding
+  uint32_t* ctr;         // [2][32] work counters: finished waves, the tail's tickets
   int64_t max_items;
 };
 

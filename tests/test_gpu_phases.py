@@ -50,10 +50,11 @@ def test_plan_reused_across_layers(kv4, fmt):
 
 @pytest.mark.parametrize("fmt", [0, 1], ids=["kv4", "kv8"])
 def test_attend_repeated_on_one_plan(kv4, fmt):
-    """A plan is read, never consumed, by the attention phase (its unit
-    counter lives in LDS and starts at zero in every launch): many ATTEND +
-    MERGE pairs on one PLAN, with different queries in between, each give the
-    bits of a full decode."""
+    """A plan is read, never consumed, by the attention phase (the per-CU
+    ticket counters live in LDS and start at zero in every launch; the last
+    wave of a launch zeroes the device counter of the list's tail): many
+    ATTEND + MERGE pairs on one PLAN, with different queries in between, each
+    give the bits of a full decode."""
     import torch
 
     from harness import build_config
@@ -77,3 +78,39 @@ def test_attend_repeated_on_one_plan(kv4, fmt):
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.int16), ref_out.view(torch.int16)), rep
         assert torch.equal(lse.view(torch.int32), ref_lse.view(torch.int32)), rep
+
+
+@pytest.mark.parametrize("fmt", [0, 2], ids=["kv4", "bf16"])
+def test_attend_twice_without_merge(kv4, fmt):
+    """ATTEND with one query, ATTEND again with another, then MERGE: the
+    result is the second query's full decode, bit for bit.  Every unit of the
+    second launch must run, including those of the list's tail, which are
+    drawn from a device counter that the first launch's last wave resets; a
+    unit that did not run would keep the first query's values."""
+    import torch
+
+    from harness import build_config
+
+    wl = build_config(1, fmt)
+    wl.step_append()
+    ws = torch.empty_like(wl.workspace)
+    ws.fill_(0x5A)
+    kv4.decode_phases(wl.cache, wl.batch, None, None, None, ws, kv4.PHASE_PLAN)
+    header = ws[:16].view(torch.int32).cpu()
+    nitems, cus = int(header[1]), torch.cuda.get_device_properties(0).multi_processor_count
+    assert nitems - (nitems - nitems // 4) // cus * cus > 0, "the workload has no tail"
+    gen = torch.Generator(device="cpu").manual_seed(12)
+    q1 = (torch.randn(wl.q.shape, generator=gen) * 3).to(torch.bfloat16).to("cuda")
+    q2 = torch.randn(wl.q.shape, generator=gen).to(torch.bfloat16).to("cuda")
+    wl.q.copy_(q2)
+    wl.decode()
+    torch.cuda.synchronize()
+    ref_out, ref_lse = wl.out.clone(), wl.lse.clone()
+    out = torch.full_like(wl.out, float("nan"))
+    lse = torch.full_like(wl.lse, float("nan"))
+    kv4.decode_phases(wl.cache, wl.batch, q1, out, lse, ws, kv4.PHASE_ATTEND)
+    kv4.decode_phases(wl.cache, wl.batch, q2, out, lse, ws, kv4.PHASE_ATTEND)
+    kv4.decode_phases(wl.cache, wl.batch, q2, out, lse, ws, kv4.PHASE_MERGE)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), ref_out.view(torch.int16))
+    assert torch.equal(lse.view(torch.int32), ref_lse.view(torch.int32))
