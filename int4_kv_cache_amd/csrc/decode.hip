@@ -47,7 +47,7 @@ constexpr int kChunkPages = 32;        // smallest chunk of middle pages per wor
 constexpr int kWavesPerEU = 2;         // attention waves per SIMD (215 of 256 registers)
 constexpr int kStages4 = 2;            // register pipeline depth of the INT4 page loop (3 and 4: 1% slower)
 constexpr int kStages8 = 2;            // pipeline depth of the INT8 tile loops; bf16 tiles use 1
-constexpr int kUnitsPerWave = 6;       // work-list granularity: chunk size from the total work
+constexpr int kUnitsPerWave = 4;       // work-list granularity: chunk size from the total work
 constexpr int kMergeK = 4;             // partial rows a merge task loads per round (8: 104 registers, slower)
 constexpr int kMaxChunkPages = 128;    // largest chunk of the single-query kernel (two page ids per lane)
 constexpr float kLog2e = 1.4426950408889634f;

@@ -200,7 +200,7 @@ def test_config2_full_size_bench_launch(kv4):
 @pytest.mark.parametrize("fmt,S,R", [(1, 0, 0), (2, 0, 0), (0, 0, 0)], ids=["kv8", "bf16", "int4_plain"])
 def test_config2_full_size_variants(kv4, fmt, S, R):
     """The reference variants of the precision ablation at the config-2 batch
-    (1,024 sequences, chunks of about 97 pages), through the benchmark's launch
+    (1,024 sequences, chunks of the largest size, 128 pages), through the benchmark's launch
     sequence, against the oracle on sampled sequences."""
     from harness import build_config
 
