@@ -180,13 +180,24 @@ __device__ inline float quad_reduce_scatter(const float (&x)[4], int lane) {
 template <int KIND, int D>
 struct LaneOff {
   uint32_t k, v, ks, vs;
-  __device__ inline LaneOff(int ln, int kg) {
+  uint32_t sc;      // INT4, D = 128: this lane's dword of the scale area
+  int src[4];       // INT4, D = 128: ds_bpermute addresses of K0, K1, V0, V1
+  __device__ inline LaneOff(int ln, int kg) : sc(0), src{0, 0, 0, 0} {
     constexpr int NG = D / 32;
     if constexpr (KIND == kInt4Page) {
       k = ln * (D / 2) + kg * (D / 8);
       v = 8 * D + (kg * 16 + ln) * (D / 8);
       ks = 16 * D + ((ln % NG) * 16 + kg * 4) * 2;
       vs = ks + D;
+      // At D = 128 the four lanes kg * 16 + g + 4j (j = 0..3, one query head
+      // each) need the same scales: group g of positions 4kg..4kg+3, two K
+      // dwords and two V dwords.  Lane j of them loads dword j only (every
+      // lane one distinct dword of the 256-byte scale area) and each lane
+      // gathers the four from its group (ds_bpermute addresses in src).
+      const int j = ln >> 2;
+      sc = (j < 2 ? ks : vs) + 4 * (j & 1);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) src[i] = 4 * (kg * 16 + (ln % NG) + 4 * i);
     } else if constexpr (KIND == kInt8Tile) {
       k = ln * D + kg * (D / 4);
       v = 16 * D + (kg * 16 + ln) * (D / 4);
@@ -231,6 +242,11 @@ __device__ inline uint2 ld8(const TileSrc& t, uint32_t off) {
   return make_uint2(r.x, r.y);
 }
 
+template <bool NT>
+__device__ inline uint32_t ld4(const TileSrc& t, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(t.r, off, 0, NT ? 2 : 0);
+}
+
 template <int KIND, int D>
 struct Tile;
 
@@ -240,6 +256,7 @@ struct Tile<kInt4Page, D> {
   uint32_t k[KW];
   uint32_t v[KW];
   uint32_t ks[2], vs[2];  // fp16 scales of positions 4kg..4kg+3, group = ln % NG
+  uint32_t sc;            // D = 128: this lane's dword of the scales, until `gather`
   static constexpr int kBytes = int(int4_block_bytes(D));
   template <bool NT>
   __device__ inline void load(const TileSrc& blk, const LaneOff<kInt4Page, D>& o) {
@@ -248,16 +265,30 @@ struct Tile<kInt4Page, D> {
       const uint4 b = ld16<NT>(blk, o.v);
       k[0] = a.x; k[1] = a.y; k[2] = a.z; k[3] = a.w;
       v[0] = b.x; v[1] = b.y; v[2] = b.z; v[3] = b.w;
+      // one dword per lane: the texture path moves every lane's bytes, and
+      // the 8-byte scale loads of the four lanes sharing them cost a third of
+      // a tile's load time
+      sc = ld4<NT>(blk, o.sc);
     } else {
       const uint2 a = ld8<NT>(blk, o.k);
       const uint2 b = ld8<NT>(blk, o.v);
       k[0] = a.x; k[1] = a.y;
       v[0] = b.x; v[1] = b.y;
+      const uint2 s = ld8<NT>(blk, o.ks);
+      const uint2 t = ld8<NT>(blk, o.vs);
+      ks[0] = s.x; ks[1] = s.y;
+      vs[0] = t.x; vs[1] = t.y;
     }
-    const uint2 s = ld8<NT>(blk, o.ks);
-    const uint2 t = ld8<NT>(blk, o.vs);
-    ks[0] = s.x; ks[1] = s.y;
-    vs[0] = t.x; vs[1] = t.y;
+  }
+  // After the loads have arrived: each lane's scales from the lanes that
+  // loaded them.
+  __device__ inline void gather(const LaneOff<kInt4Page, D>& o) {
+    if constexpr (KW == 4) {
+      ks[0] = uint32_t(__builtin_amdgcn_ds_bpermute(o.src[0], int(sc)));
+      ks[1] = uint32_t(__builtin_amdgcn_ds_bpermute(o.src[1], int(sc)));
+      vs[0] = uint32_t(__builtin_amdgcn_ds_bpermute(o.src[2], int(sc)));
+      vs[1] = uint32_t(__builtin_amdgcn_ds_bpermute(o.src[3], int(sc)));
+    }
   }
 };
 
@@ -282,6 +313,7 @@ struct Tile<kInt8Tile, D> {
     ks[0] = s.x; ks[1] = s.y;
     vs[0] = t.x; vs[1] = t.y;
   }
+  __device__ inline void gather(const LaneOff<kInt8Tile, D>&) {}
 };
 
 template <int D>
@@ -300,6 +332,7 @@ struct Tile<kBf16Page, D> {
       v[4 * i] = b.x; v[4 * i + 1] = b.y; v[4 * i + 2] = b.z; v[4 * i + 3] = b.w;
     }
   }
+  __device__ inline void gather(const LaneOff<kBf16Page, D>&) {}
 };
 
 // ----------------------------------------------------------- unit state --
@@ -675,8 +708,10 @@ __device__ inline void run_tiles(Unit<D>& u, int n, PtrFn ptr, MaskFn mask, int 
     t0.template load<NT>(TileSrc(ptr(i), live ? kBytes : 0), off);
     t1.template load<NT>(TileSrc(ptr(i + 1 < n ? i + 1 : i), live && i + 1 < n ? kBytes : 0), off);
   };
-  auto run = [&](const Tile<KIND, D>& t0, const Tile<KIND, D>& t1, int s) {
+  auto run = [&](Tile<KIND, D>& t0, Tile<KIND, D>& t1, int s) {
     const int i = 2 * s;
+    t0.gather(off);
+    t1.gather(off);
     step<KIND, D, true, Q8>(u, t0, t1, mask(i), i + 1 < n ? mask(i + 1) : 0u, lane);
   };
   if constexpr (STAGES == 1) {
@@ -1397,10 +1432,6 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(kW
 // tiles at head_dim 128.  Queries see different position ranges (query t of
 // T sees [0, N - T + t + 1)), so masks are per lane (column).
 
-template <bool NT>
-__device__ inline uint32_t ld4(const TileSrc& t, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b32(t.r, off, 0, NT ? 2 : 0);
-}
 
 // Per-lane byte offsets inside a block, D = 128, lane (ln = L % 16, kg = L / 16).
 struct McOff {
