@@ -1435,11 +1435,15 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(kW
 
 // Per-lane byte offsets inside a block, D = 128, lane (ln = L % 16, kg = L / 16).
 struct McOff {
-  uint32_t k4, v4, s4, k8, v8, s8;
+  uint32_t k4, v4, s4, sc4, k8, v8, s8;
   __device__ inline McOff(int ln, int kg) {
     k4 = ln * 64 + kg * 4;               // INT4 K: + 16g -> channels 32g + 8kg .. +7 of row ln
     v4 = 8 * 128 + (kg * 16 + ln) * 16;  // INT4 V: as the single-query tile
     s4 = 16 * 128 + kg * 8;              // INT4 K scales of rows 4kg..4kg+3: + 32g; V scales + 128
+    // the 16 lanes kg * 16 + n use the same 16 scale dwords (K and V of
+    // rows 4kg..4kg+3, every group); lane n loads dword n: group n / 4,
+    // K (n % 4 < 2) or V, half n % 2
+    sc4 = s4 + 32 * (ln >> 2) + 128 * ((ln >> 1) & 1) + 4 * (ln & 1);
     k8 = ln * 128 + kg * 8;              // INT8 K: + 32g -> channels 32g + 8kg .. +7 of row ln
     v8 = 16 * 128 + (kg * 16 + ln) * 32; // INT8 V: as the single-query tile
     s8 = 32 * 128 + kg * 8;              // INT8 K scales of rows 4kg..4kg+3; V scales + 32
@@ -1454,19 +1458,34 @@ struct McTile<kInt4Page> {
   static constexpr int kBytes = int(int4_block_bytes(128));
   uint32_t k[4];      // group g: channels 32g + 8kg .. +7 of row ln (8 nibbles)
   uint32_t v[4];      // V codes, the single-query tile's layout
-  uint32_t ks[4][2];  // group g: fp16 K scales of rows 4kg..4kg+3
+  uint32_t ks[4][2];  // group g: fp16 K scales of rows 4kg..4kg+3 (after `gather`)
   uint32_t vs[4][2];
+  uint32_t sc;        // this lane's dword of the scale area, until `gather`
   __device__ inline void load(const TileSrc& s, const McOff& o) {
 #pragma unroll
     for (int g = 0; g < 4; ++g) k[g] = ld4<false>(s, o.k4 + 16 * g);
     const uint4 a = ld16<false>(s, o.v4);
     v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    // one distinct dword per lane: with each lane loading its 64 bytes of
+    // scales itself, two thirds of the bytes a tile moves through the
+    // texture path were scale loads repeated by the 16 lanes of a row
+    sc = ld4<false>(s, o.sc4);
+  }
+  // After the loads have arrived: the wave's 64 scale dwords pass through its
+  // own 256-byte LDS slot, and each lane reads its row's 16 (group g: K
+  // halves at 4g, 4g + 1, V halves at 4g + 2, 4g + 3).  The exchange stays
+  // within the wave, whose LDS operations complete in order.
+  __device__ inline void gather(uint32_t* slot, int lane) {
+    slot[lane] = sc;
+    __builtin_amdgcn_wave_barrier();
+    const uint32_t* row = slot + (lane >> 4) * 16;
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const uint2 x = ld8<false>(s, o.s4 + 32 * g), y = ld8<false>(s, o.s4 + 128 + 32 * g);
+      const uint4 x = *reinterpret_cast<const uint4*>(row + 4 * g);
       ks[g][0] = x.x; ks[g][1] = x.y;
-      vs[g][0] = y.x; vs[g][1] = y.y;
+      vs[g][0] = x.z; vs[g][1] = x.w;
     }
+    __builtin_amdgcn_wave_barrier();
   }
 };
 
@@ -1491,6 +1510,7 @@ struct McTile<kInt8Tile> {
     ks[0] = x.x; ks[1] = x.y;
     vs[0] = y.x; vs[1] = y.y;
   }
+  __device__ inline void gather(uint32_t*, int) {}
 };
 
 struct McUnit {
@@ -1661,8 +1681,14 @@ __device__ inline void run_mc(McUnit& u, int n, PtrFn ptr, MaskFn mask, int lane
     t0.load(TileSrc(ptr(i), live ? kBytes : 0), off);
     t1.load(TileSrc(ptr(i + 1 < n ? i + 1 : i), live && i + 1 < n ? kBytes : 0), off);
   };
-  auto run = [&](const McTile<KIND>& t0, const McTile<KIND>& t1, int s) {
+  // per-wave LDS slots of the scale exchange, one per tile of a step
+  __shared__ uint32_t scale_slots[kAttnThreads / kWave][2][kWave];
+  uint32_t* slot0 = scale_slots[threadIdx.x / kWave][0];
+  uint32_t* slot1 = scale_slots[threadIdx.x / kWave][1];
+  auto run = [&](McTile<KIND>& t0, McTile<KIND>& t1, int s) {
     const int i = 2 * s;
+    t0.gather(slot0, lane);
+    t1.gather(slot1, lane);
     step_mc<KIND>(u, t0, t1, mask(i), i + 1 < n ? mask(i + 1) : 0u, lane);
   };
   // one stage: a second one measured 1.3% slower (registers)
