@@ -181,8 +181,8 @@ template <int KIND, int D>
 struct LaneOff {
   uint32_t k, v, ks, vs;
   uint32_t sc;      // INT4, D = 128: this lane's dword of the scale area
-  int src[4];       // INT4, D = 128: ds_bpermute addresses of K0, K1, V0, V1
-  __device__ inline LaneOff(int ln, int kg) : sc(0), src{0, 0, 0, 0} {
+  int put, get;     // INT4, D = 128: where it goes in the wave's LDS slot, where the lane's four are
+  __device__ inline LaneOff(int ln, int kg) : sc(0), put(0), get(0) {
     constexpr int NG = D / 32;
     if constexpr (KIND == kInt4Page) {
       k = ln * (D / 2) + kg * (D / 8);
@@ -196,8 +196,9 @@ struct LaneOff {
       // gathers the four from its group (ds_bpermute addresses in src).
       const int j = ln >> 2;
       sc = (j < 2 ? ks : vs) + 4 * (j & 1);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) src[i] = 4 * (kg * 16 + (ln % NG) + 4 * i);
+      // LDS slot positions: the group's four dwords next to each other
+      put = kg * 16 + (ln % NG) * 4 + j;
+      get = kg * 16 + (ln % NG) * 4;
     } else if constexpr (KIND == kInt8Tile) {
       k = ln * D + kg * (D / 4);
       v = 16 * D + (kg * 16 + ln) * (D / 4);
@@ -281,13 +282,16 @@ struct Tile<kInt4Page, D> {
     }
   }
   // After the loads have arrived: each lane's scales from the lanes that
-  // loaded them.
-  __device__ inline void gather(const LaneOff<kInt4Page, D>& o) {
+  // loaded them, through the wave's own 256-byte LDS slot (the exchange stays
+  // within the wave, whose LDS operations complete in order).
+  __device__ inline void gather(const LaneOff<kInt4Page, D>& o, uint32_t* slot) {
     if constexpr (KW == 4) {
-      ks[0] = uint32_t(__builtin_amdgcn_ds_bpermute(o.src[0], int(sc)));
-      ks[1] = uint32_t(__builtin_amdgcn_ds_bpermute(o.src[1], int(sc)));
-      vs[0] = uint32_t(__builtin_amdgcn_ds_bpermute(o.src[2], int(sc)));
-      vs[1] = uint32_t(__builtin_amdgcn_ds_bpermute(o.src[3], int(sc)));
+      slot[o.put] = sc;
+      __builtin_amdgcn_wave_barrier();
+      const uint4 x = *reinterpret_cast<const uint4*>(slot + o.get);
+      __builtin_amdgcn_wave_barrier();
+      ks[0] = x.x; ks[1] = x.y;
+      vs[0] = x.z; vs[1] = x.w;
     }
   }
 };
@@ -313,7 +317,7 @@ struct Tile<kInt8Tile, D> {
     ks[0] = s.x; ks[1] = s.y;
     vs[0] = t.x; vs[1] = t.y;
   }
-  __device__ inline void gather(const LaneOff<kInt8Tile, D>&) {}
+  __device__ inline void gather(const LaneOff<kInt8Tile, D>&, uint32_t*) {}
 };
 
 template <int D>
@@ -332,7 +336,7 @@ struct Tile<kBf16Page, D> {
       v[4 * i] = b.x; v[4 * i + 1] = b.y; v[4 * i + 2] = b.z; v[4 * i + 3] = b.w;
     }
   }
-  __device__ inline void gather(const LaneOff<kBf16Page, D>&) {}
+  __device__ inline void gather(const LaneOff<kBf16Page, D>&, uint32_t*) {}
 };
 
 // ----------------------------------------------------------- unit state --
@@ -708,10 +712,14 @@ __device__ inline void run_tiles(Unit<D>& u, int n, PtrFn ptr, MaskFn mask, int 
     t0.template load<NT>(TileSrc(ptr(i), live ? kBytes : 0), off);
     t1.template load<NT>(TileSrc(ptr(i + 1 < n ? i + 1 : i), live && i + 1 < n ? kBytes : 0), off);
   };
+  // per-wave LDS slots of the scale exchange, one per tile of a step
+  __shared__ uint32_t sq_slots[kAttnThreads / kWave][2][kWave];
+  uint32_t* slot0 = sq_slots[threadIdx.x / kWave][0];
+  uint32_t* slot1 = sq_slots[threadIdx.x / kWave][1];
   auto run = [&](Tile<KIND, D>& t0, Tile<KIND, D>& t1, int s) {
     const int i = 2 * s;
-    t0.gather(off);
-    t1.gather(off);
+    t0.gather(off, slot0);
+    t1.gather(off, slot1);
     step<KIND, D, true, Q8>(u, t0, t1, mask(i), i + 1 < n ? mask(i + 1) : 0u, lane);
   };
   if constexpr (STAGES == 1) {
