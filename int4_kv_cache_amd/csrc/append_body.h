@@ -144,9 +144,20 @@ __device__ inline void append_row(const AppendParams& p, int64_t w) {
     kb[e] = kr[e];
     vb[e] = vr[e];
   }
-  const int b = find_seq(p.cu_new, p.batch, t, lane);
-  const int nb = p.cu_new[b + 1] - p.cu_new[b];
-  const int pos = p.seq_lens[b] - nb + (t - p.cu_new[b]);
+  // The sequence of token t: first the guess for equal token counts per
+  // sequence (one token each in a decode step), whose cu_new entries,
+  // length and slot are loaded together; a search when the guess is wrong.
+  int b = int(int64_t(t) * p.batch / p.total_new);
+  int c0 = p.cu_new[b], c1 = p.cu_new[b + 1], len = p.seq_lens[b];
+  int slot = p.slot_ids ? p.slot_ids[b] : b;
+  if (!(c0 <= t && t < c1)) {  // wave-uniform
+    b = find_seq(p.cu_new, p.batch, t, lane);
+    c0 = p.cu_new[b];
+    c1 = p.cu_new[b + 1];
+    len = p.seq_lens[b];
+    slot = p.slot_ids ? p.slot_ids[b] : b;
+  }
+  const int pos = len - (c1 - c0) + (t - c0);
   if (pos < 0 || pos >= p.max_pages * kPage) return;  // outside the page table: skipped
   const int64_t pid = p.page_table[int64_t(b) * p.max_pages + pos / kPage];
   if (pid < 0 || pid >= p.num_pages) return;
@@ -165,8 +176,7 @@ __device__ inline void append_row(const AppendParams& p, int64_t w) {
     // A ring row is written only by a position that is still among the last R
     // after this call, so positions of one call never share a ring row (the
     // result equals appending the tokens one at a time).
-    if (pos < S || (R > 0 && pos >= p.seq_lens[b] - R)) {
-      const int slot = p.slot_ids ? p.slot_ids[b] : b;
+    if (pos < S || (R > 0 && pos >= len - R)) {
       if (slot >= 0 && slot < p.num_slots) {
         const int row = side_row(pos, S, R);
         uint8_t* tile = p.side + (int64_t(slot) * H + h) * int64_t(p.side_bytes) +
