@@ -897,8 +897,10 @@ __device__ inline void plan_body(const DecodeParams& p, int units_per_item) {
   cl = cl < unsigned(kChunkPages) ? unsigned(kChunkPages) : (cl > cmax ? cmax : cl);
   const int chunk = int(cl);
 
-  // pass 1: full items (scan) and the histogram of the other items' sizes
-  int run_full = 0, run_split = 0;
+  // pass 1: full items (scan) and the histogram of the other items' sizes;
+  // the first sequence's partial slot and first full-item position are also
+  // kept in registers for pass 2
+  int run_full = 0, run_split = 0, pbase0 = 0, fpos0 = 0;
   for (int base = 0; base < nv; base += 1024) {
     const int b = base + tid;
     int full = 0, split = 0;
@@ -917,7 +919,11 @@ __device__ inline void plan_body(const DecodeParams& p, int units_per_item) {
         block_exclusive_scan((unsigned long long)full | ((unsigned long long)split << 32), part, tile);
     if (b < nv) {
       p.ws.item_base[b] = run_split + int(ex >> 32);
-      p.ws.merge_list[b] = run_full + int(ex & 0xFFFFFFFFull);  // scratch: first full-item position
+      p.ws.merge_list[b].x = run_full + int(ex & 0xFFFFFFFFull);  // scratch: first full-item position
+      if (base == 0) {
+        pbase0 = run_split + int(ex >> 32);
+        fpos0 = run_full + int(ex & 0xFFFFFFFFull);
+      }
     }
     run_full += int(tile & 0xFFFFFFFFull);
     run_split += int(tile >> 32);
@@ -952,20 +958,22 @@ __device__ inline void plan_body(const DecodeParams& p, int units_per_item) {
   for (int b = tid; b < nv; b += 1024) {
     const SeqWork w = b == tid ? w0 : seq_work(p, b);
     const int n = n_items(w, chunk);
-    const int pbase = p.ws.item_base[b];
-    uint32_t fpos = uint32_t(p.ws.merge_list[b]);
+    const int pbase = b == tid ? pbase0 : p.ws.item_base[b];
+    uint32_t fpos = uint32_t(b == tid ? fpos0 : p.ws.merge_list[b].x);
     for (int k = 0; k < n; ++k) {
       const int pg = item_pages(w, chunk, k);
       const uint32_t pos = pg == chunk ? fpos++ : atomicAdd(&bucket[kMaxChunkPages - item_key(w, chunk, k)], 1u);
       write_item(p, pos, b, w, chunk, k, n, pbase);
     }
-    p.ws.item_count[b] = n;
   }
   __syncthreads();
-  // list of split sequences for the merge (overwrites the scratch use above)
+  // records of the split sequences for the merge (overwrite the scratch use
+  // above): the merge loads one record instead of the list entry and then
+  // the sequence's slot and item count
   for (int b = tid; b < nv; b += 1024) {
     const SeqWork w = b == tid ? w0 : seq_work(p, b);
-    if (n_items(w, chunk) > 1) p.ws.merge_list[atomicAdd(&nmerge, 1u)] = b;
+    const int n = n_items(w, chunk);
+    if (n > 1) p.ws.merge_list[atomicAdd(&nmerge, 1u)] = make_int4(b, b == tid ? pbase0 : p.ws.item_base[b], n, 0);
   }
   __syncthreads();
   if (tid == 0) p.ws.header[3] = nmerge;
@@ -1893,14 +1901,21 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeParams p) {
   const int64_t nt = int64_t(gridDim.x) * (blockDim.x / QL);
   const int nqb = n_blocks(p);
   const int64_t per = int64_t(p.tq) * Hq;  // (query of the block, head) pairs
+  // A task's record is loaded before the count of split sequences is known
+  // (the index clamped to the list's extent, the work blocks), so the two
+  // loads overlap; a record past the count is never used.
+  const int64_t last = int64_t(p.batch) * nqb - 1;
+  auto record = [&](int64_t w) { return p.ws.merge_list[w / per < last ? w / per : last]; };
+  int64_t w = int64_t(blockIdx.x) * (blockDim.x / QL) + threadIdx.x / QL;
+  int4 rec = record(w);
   const int64_t tasks = int64_t(p.ws.header[3]) * per;
-  for (int64_t w = int64_t(blockIdx.x) * (blockDim.x / QL) + threadIdx.x / QL; w < tasks; w += nt) {
-    const int u = p.ws.merge_list[w / per];
+  for (; w < tasks; w += nt, rec = record(w)) {
+    const int u = rec.x;
     const int j = int((w % per) / Hq), hq = int(w % Hq);
     if (j >= block_queries(p, u)) continue;
     const int b = (u / nqb) * p.nq + (u % nqb) * p.tq + j;  // output row: query t of sequence b
-    const int n = p.ws.item_count[u];
-    const float* base = p.ws.partials + ((int64_t(p.ws.item_base[u]) + int64_t(j) * n) * Hq + hq) * RS;
+    const int n = rec.z;
+    const float* base = p.ws.partials + ((int64_t(rec.y) + int64_t(j) * n) * Hq + hq) * RS;
     const int64_t stride = int64_t(Hq) * RS;
     float M = -INFINITY, l = 0.f, o[E];
 #pragma unroll
@@ -2045,7 +2060,8 @@ bool decode_units_fit(int32_t batch, int32_t max_pages, int32_t num_q_heads, int
 size_t decode_workspace_bytes(int32_t batch, int32_t max_pages, int32_t num_q_heads, int32_t head_dim) {
   const int64_t max_items = max_items_of(batch, max_pages);
   size_t s = 256;                                   // header
-  s += 3 * align256(sizeof(int32_t) * size_t(batch));  // item_base, item_count, merge_list
+  s += align256(sizeof(int32_t) * size_t(batch));      // item_base
+  s += align256(sizeof(int4) * size_t(batch));         // merge_list
   s += align256(2 * sizeof(int4) * size_t(max_items)); // items
   s += align256(sizeof(float) * size_t(max_items) * num_q_heads * part_stride(head_dim));
   s += 2 * kCtrStride * sizeof(uint32_t);  // work counters
@@ -2061,10 +2077,8 @@ DecodeWorkspace carve_workspace(void* base, int32_t batch, int32_t max_pages, in
   q += 256;
   w.item_base = reinterpret_cast<int32_t*>(q);
   q += align256(sizeof(int32_t) * size_t(batch));
-  w.item_count = reinterpret_cast<int32_t*>(q);
-  q += align256(sizeof(int32_t) * size_t(batch));
-  w.merge_list = reinterpret_cast<int32_t*>(q);
-  q += align256(sizeof(int32_t) * size_t(batch));
+  w.merge_list = reinterpret_cast<int4*>(q);
+  q += align256(sizeof(int4) * size_t(batch));
   w.items = reinterpret_cast<int4*>(q);
   q += align256(2 * sizeof(int4) * size_t(max_items));
   w.partials = reinterpret_cast<float*>(q);

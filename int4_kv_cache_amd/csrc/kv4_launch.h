@@ -29,14 +29,13 @@ struct AppendParams {
 
 hipError_t launch_append(int fmt, const AppendParams& p, int head_dim, hipStream_t stream);
 
-// Decode workspace: a header, per-sequence item table, the work items
-// (costliest first), the list of sequences split over several items and the
-// fp32 partial results of those items.
+// Decode workspace: a header, the first partial slot of every sequence, the
+// records of the sequences split over several items, the work items
+// (costliest first) and the fp32 partial results of the split items.
 struct DecodeWorkspace {
   uint32_t* header;      // [0] unused, [1] items, [2] chunk pages, [3] split sequences
   int32_t* item_base;    // [batch] first partial slot of a split sequence
-  int32_t* item_count;   // [batch]
-  int32_t* merge_list;   // [batch] split sequences
+  int4* merge_list;      // [batch] split sequences: {work index, first partial slot, items, 0}
   int4* items;           // [max_items][2] work-item descriptors (two int4 each)
   float* partials;       // [max_items][num_q_heads][head_dim + 4]: o, m, l, padding
   uint32_t* ctr;         // [2][32] work counters: finished waves, the tail's tickets
