@@ -345,7 +345,7 @@ kv4_status kvbf16_decode_attention_mq(const kv4_layout* layout, const kv4_cache*
  * nor host memory.  A batch whose kv4_decode_workspace_size exceeds
  * KV4_NOALLOC_SCRATCH_BYTES is rejected with KV4_ERR_WORKSPACE before
  * anything is launched (about 3,900 work items at 32 query heads and
- * head_dim 128, e.g. 118 sequences with page tables of 1,040 columns).
+ * head_dim 128, e.g. 120 sequences with page tables of 1,040 columns).
  * Every call on one GPU uses that GPU's one array: calls that overlap on a
  * GPU (other streams, other host threads) race and must be ordered by the
  * caller.  The array's contents are never read before a call writes them, so
